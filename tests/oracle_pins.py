@@ -1,0 +1,379 @@
+"""Checks that pin the CPU oracle to something other than itself.
+
+Each check takes the oracle module as an argument so the same checks can be run against
+deliberately broken copies of it (see test_oracle_mutants.py). A check raises
+AssertionError when the oracle disagrees with:
+  * values worked by hand from the pages (tests/golden/*.json, each with its citation),
+  * numpy library routines the step reduces to (fancy-index gather, index-put scatter),
+  * brute-force element loops over the semantic 5-D layout (no byte-offset arithmetic),
+  * invariants that hold for any input (run expansion, maximality, round trip).
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _tagged_caches(num_layers, num_blocks, block_bytes):
+    """Every byte of block b in layer l holds 10*l + b."""
+    return [np.repeat((10 * l + np.arange(num_blocks)).astype(np.uint8)[:, None], block_bytes, 1)
+            for l in range(num_layers)]
+
+
+# --------------------------------------------------------------------------- slot mapping
+
+def pin_slot_golden(o):
+    for case in _golden("slot_mapping_cases.json")["cases"]:
+        bt = np.array(case["block_table"], np.int32)
+        slots, err = o.slot_mapping(bt, case["req_idx"], case["positions"], case["block_size"])
+        assert slots.tolist() == case["expected"], case["name"]
+        assert err == case.get("expected_err", 0), case["name"]
+
+
+def pin_slot_owner_brute_force(o):
+    """Walk every slot of every listed block and record which (request, position) owns it;
+    each token's slot must be owned by that token."""
+    d = W.decode_write(seed=5, num_reqs=6, max_len=70, num_blocks=64, num_kv_heads=1,
+                       head_dim=8, with_values=False)
+    bs = d.spec.block_size
+    owner = {}
+    for r, ids in enumerate(d.tables):
+        pos = 0
+        for b in ids:
+            for t in range(bs):
+                owner[int(b) * bs + t] = (r, pos)
+                pos += 1
+    slots, err = o.slot_mapping(d.block_table, d.req_idx, d.positions, bs)
+    assert err == 0
+    for i in range(len(slots)):
+        assert owner[int(slots[i])] == (int(d.req_idx[i]), int(d.positions[i]))
+    assert len(set(slots.tolist())) == len(slots)  # disjoint tables -> unique slots
+
+
+# --------------------------------------------------------------------------- new-token write
+
+def _decode_case(seed, H, D, num_blocks=48, num_reqs=5, max_len=60):
+    d = W.decode_write(seed=seed, num_reqs=num_reqs, max_len=max_len, num_blocks=num_blocks,
+                       num_kv_heads=H, head_dim=D)
+    return d
+
+
+def pin_reshape_readback_blocks_first(o):
+    """[blocks][tokens][K,V][H][D]: read every token back through the 5-D view."""
+    d = _decode_case(11, H=2, D=8)
+    s = d.spec
+    slots, _ = o.slot_mapping(d.block_table, d.req_idx, d.positions, s.block_size)
+    cache = np.full(s.shape5, W.SENTINEL16, np.uint16)
+    row = s.row_bytes
+    out, err = o.reshape_and_cache(cache, d.key, d.value, slots, s.num_blocks, s.block_size,
+                                   s.block_size * 2 * row, 2 * row, row)
+    assert err == 0
+    v5 = out.view(np.uint16).reshape(s.shape5)
+    touched = np.zeros(s.shape5[:3], bool)
+    for i, sl in enumerate(slots):
+        b, t = divmod(int(sl), s.block_size)
+        assert np.array_equal(v5[b, t, 0], d.key[i]) and np.array_equal(v5[b, t, 1], d.value[i])
+        touched[b, t, :] = True
+    assert np.all(v5[~touched] == W.SENTINEL16)
+    assert touched.sum() == 2 * len(slots)
+
+
+def pin_reshape_element_loop_kv_inner_layout(o):
+    """(blocks, K/V, tokens, H, D) layout, element by element."""
+    d = _decode_case(12, H=2, D=4, num_blocks=40, num_reqs=4, max_len=50)
+    s = d.spec
+    nb, bs, H, D = s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim
+    slots, _ = o.slot_mapping(d.block_table, d.req_idx, d.positions, bs)
+    cache = np.full((nb, 2, bs, H, D), W.SENTINEL16, np.uint16)
+    row = H * D * 2
+    out, err = o.reshape_and_cache(cache, d.key, d.value, slots, nb, bs, 2 * bs * row, row, bs * row)
+    v = out.view(np.uint16).reshape(nb, 2, bs, H, D)
+    expect = np.full_like(v, W.SENTINEL16)
+    for i, sl in enumerate(slots):
+        b, t = int(sl) // bs, int(sl) % bs
+        for h in range(H):
+            for e in range(D):
+                expect[b, 0, t, h, e] = d.key[i, h, e]
+                expect[b, 1, t, h, e] = d.value[i, h, e]
+    assert err == 0 and np.array_equal(v, expect)
+
+
+def pin_reshape_kv_first_layout(o):
+    """(K/V, blocks, tokens, H, D): the K and V planes are a whole cache apart."""
+    d = _decode_case(13, H=1, D=8, num_blocks=40, num_reqs=4, max_len=50)
+    s = d.spec
+    nb, bs = s.num_blocks, s.block_size
+    slots, _ = o.slot_mapping(d.block_table, d.req_idx, d.positions, bs)
+    cache = np.full((2, nb, bs, 1, 8), W.SENTINEL16, np.uint16)
+    row = 16
+    out, err = o.reshape_and_cache(cache, d.key, d.value, slots, nb, bs, bs * row, row, nb * bs * row)
+    v = out.view(np.uint16).reshape(2, nb, bs, 1, 8)
+    for i, sl in enumerate(slots):
+        b, t = divmod(int(sl), bs)
+        assert np.array_equal(v[0, b, t], d.key[i]) and np.array_equal(v[1, b, t], d.value[i])
+    assert err == 0
+
+
+def pin_reshape_padding_and_range(o):
+    """Negative slots are skipped silently; slots past the cache are skipped and flagged;
+    later tokens overwrite earlier ones in token order."""
+    cache = np.zeros((4, 2, 2, 1, 8), np.uint16)  # 4 blocks of 2 tokens, row = 16 B
+    key = np.arange(4 * 8, dtype=np.uint16).reshape(4, 1, 8) + 1
+    val = key + 100
+    slots = [-1, 8, 3, 3]
+    out, err = o.reshape_and_cache(cache, key, val, slots, 4, 2, 64, 32, 16)
+    v = out.view(np.uint16).reshape(4, 2, 2, 1, 8)
+    assert err == o.DEVERR_SLOT_RANGE
+    assert np.array_equal(v[1, 1, 0], key[3]) and np.array_equal(v[1, 1, 1], val[3])
+    v[1, 1] = 0
+    assert not v.any()
+
+
+# --------------------------------------------------------------------------- runs
+
+def pin_xfer_golden(o):
+    g = _golden("transfer_hw4.json")
+    src = [np.array(t) for t in g["src_tables"]]
+    dst = [np.array(t) for t in g["dst_tables"]]
+    for mode, key in ((o.MODE_PACK, "runs_pack"), (o.MODE_UNPACK, "runs_unpack"),
+                      (o.MODE_DIRECT, "runs_direct")):
+        got = [list(x) for x in o.xfer_list(src, dst, mode)]
+        assert got == g[key], key
+
+
+def check_runs(runs, src_tables, dst_tables, mode):
+    """Invariants any correct run list satisfies."""
+    uses_src = mode in (0, 2)
+    uses_dst = mode in (1, 2)
+    flat_src = np.concatenate(src_tables) if uses_src else None
+    flat_dst = np.concatenate(dst_tables) if uses_dst else None
+    req_of = np.concatenate([np.full(len(t), r) for r, t in enumerate(src_tables if uses_src else dst_tables)])
+    N = len(req_of)
+    assert sum(n for *_, n, _ in runs) == N
+    assert len(runs) <= N
+    covered = 0
+    for (s, d, b, n, r) in runs:
+        assert b == covered and n >= 1
+        assert np.all(req_of[b:b + n] == r)
+        if uses_src:
+            assert np.array_equal(flat_src[b:b + n], s + np.arange(n))
+        else:
+            assert s == b
+        if uses_dst:
+            assert np.array_equal(flat_dst[b:b + n], d + np.arange(n))
+        else:
+            assert d == b
+        covered += n
+    # maximal: the block after a run is in another request or breaks the +1 step
+    for (s, d, b, n, r) in runs:
+        e = b + n
+        if e < N and req_of[e] == r:
+            breaks = (uses_src and flat_src[e] != flat_src[e - 1] + 1) or \
+                     (uses_dst and flat_dst[e] != flat_dst[e - 1] + 1)
+            assert breaks
+
+
+def pin_xfer_invariants(o):
+    for seed in range(4):
+        c = W.random_transfer(seed, 1, 600, 4, 1, 2, [5, 0, 61, 17, 1, 230], with_caches=False)
+        for mode in (o.MODE_PACK, o.MODE_UNPACK, o.MODE_DIRECT):
+            check_runs(o.xfer_list(c.src_tables, c.dst_tables, mode), c.src_tables, c.dst_tables, mode)
+
+
+def pin_xfer_pages_contiguous_count(o):
+    """Runs of 64 in their own slots: at most 9 runs per 576-block request (72 in all)."""
+    c = W.pages_contiguous(num_layers=1)
+    runs = o.xfer_list(c.src_tables, c.dst_tables, o.MODE_PACK)
+    check_runs(runs, c.src_tables, c.dst_tables, o.MODE_PACK)
+    assert len(runs) <= 72
+    assert all(n % 64 == 0 for *_, n, _ in runs)
+
+
+# --------------------------------------------------------------------------- pack
+
+def pin_pack_golden(o):
+    g = _golden("transfer_hw4.json")
+    caches = _tagged_caches(g["num_layers"], g["num_blocks"], 16)
+    buf, err = o.pack(caches, [np.array(t) for t in g["src_tables"]])
+    assert err == 0
+    assert buf.shape == (2, 6, 16)
+    assert buf[:, :, 0].tolist() == g["buffer_tags"]
+    assert np.all(buf == buf[:, :, :1])
+
+
+def pin_pack_tiny_byte_offsets(o):
+    g = _golden("byte_counts.json")["tiny_config"]
+    c = W.tiny_roundtrip()
+    bb = c.src_spec.block_bytes
+    assert bb == g["block_bytes"]
+    assert [len(t) for t in c.src_tables] == g["blocks_per_request"]
+    buf, err = o.pack(c.src_caches, c.src_tables)
+    flat = buf.reshape(-1)
+    assert flat.nbytes == g["buffer_bytes"]
+    for l in range(2):
+        layer = c.src_caches[l].reshape(64, -1).view(np.uint8)
+        for r, off in enumerate(g["request_offsets"]):
+            at = l * g["layer1_offset"] + off
+            assert np.array_equal(flat[at:at + bb], layer[c.src_tables[r][0]])
+
+
+def pin_pack_pages_volume(o):
+    """One layer of the pages' geometry (fewer blocks in the pool): 8 x 576 blocks of 8 KiB
+    give the stated per-(request, layer) and per-layer volumes."""
+    g = _golden("byte_counts.json")["pages_kv_memory"]
+    c = W.pages_contiguous(num_layers=1, num_blocks=9216, run=64)
+    spec = c.src_spec
+    assert spec.block_bytes == g["block_bytes"]
+    assert W.PagedSpec(48, 147456, 16, 1, 128).layer_bytes == g["layer_bytes"]
+    layer = np.zeros((spec.num_blocks, spec.block_bytes), np.uint8)
+    layer[:, :8] = np.arange(spec.num_blocks, dtype=np.uint64)[:, None].view(np.uint8)
+    buf, _ = o.pack([layer], c.src_tables)
+    assert buf.nbytes == g["layer_slice_bytes"]
+    assert g["request_layer_bytes"] * g["requests"] == buf.nbytes
+    ids = buf[0, :, :8].copy().view(np.uint64).reshape(-1)
+    per = g["request_layer_bytes"] // g["block_bytes"]
+    for r in range(g["requests"]):
+        assert np.array_equal(ids[r * per:(r + 1) * per], c.src_tables[r])
+
+
+def pin_pack_equals_fancy_index(o):
+    c = W.random_transfer(21, 3, 300, 4, 2, 4, [9, 40, 0, 77, 3])
+    buf, err = o.pack(c.src_caches, c.src_tables)
+    for l in range(3):
+        ref = np.concatenate([c.src_caches[l][t] for t in c.src_tables])
+        assert np.array_equal(buf[l].view(np.uint16), ref)
+
+
+def pin_pack_element_loop(o):
+    spec = W.PagedSpec(2, 12, 2, 2, 2)
+    rng = np.random.default_rng(3)
+    caches = [W.random_words(rng, spec.shape5) for _ in range(2)]
+    tables = [np.array([3, 4, 9]), np.array([0]), np.array([11, 5])]
+    buf, err = o.pack(caches, tables)
+    b5 = buf.view(np.uint16).reshape(2, 6, 2, 2, 2, 2)
+    p = 0
+    for r, t in enumerate(tables):
+        for j, blk in enumerate(t):
+            for l in range(2):
+                for tok in range(2):
+                    for kv in range(2):
+                        for h in range(2):
+                            for e in range(2):
+                                assert b5[l, p, tok, kv, h, e] == caches[l][blk, tok, kv, h, e]
+            p += 1
+
+
+def pin_pack_out_of_range(o):
+    caches = _tagged_caches(1, 4, 16)
+    buf, err = o.pack(caches, [np.array([1, 4]), np.array([-1, 2])])
+    assert err == o.DEVERR_BLOCK_RANGE
+    assert buf[0, :, 0].tolist() == [1, 0, 0, 2]
+
+
+# --------------------------------------------------------------------------- unpack
+
+def pin_unpack_golden(o):
+    g = _golden("transfer_hw4.json")
+    caches = _tagged_caches(2, 8, 16)
+    src = [np.array(t) for t in g["src_tables"]]
+    dst = [np.array(t) for t in g["dst_tables"]]
+    buf, _ = o.pack(caches, src)
+    sentinel = [np.full((8, 16), 0xEE, np.uint8) for _ in range(2)]
+    out, err = o.unpack([buf], sentinel, dst)
+    assert err == 0
+    for l in range(2):
+        got = [None if np.all(out[l][b] == 0xEE) else int(out[l][b][0]) for b in range(8)]
+        assert got == g["dst_tags_after_unpack"][l]
+
+
+def pin_unpack_equals_index_put(o):
+    c = W.random_transfer(22, 2, 200, 4, 2, 4, [13, 0, 50, 7])
+    buf, _ = o.pack(c.src_caches, c.src_tables)
+    out, err = o.unpack([buf], c.dst_caches, c.dst_tables)
+    for l in range(2):
+        ref = c.dst_caches[l].copy()
+        ref[np.concatenate(c.dst_tables)] = buf[l].view(np.uint16)
+        assert np.array_equal(out[l].view(np.uint16), ref)
+
+
+def pin_roundtrip(o):
+    c = W.tiny_roundtrip()
+    buf, _ = o.pack(c.src_caches, c.src_tables)
+    out, err = o.unpack([buf], c.dst_caches, c.dst_tables)
+    assert err == 0
+    listed = np.concatenate(c.dst_tables)
+    for l in range(2):
+        src = c.src_caches[l].reshape(64, -1)
+        got = out[l].view(np.uint16)
+        assert np.array_equal(got[listed], src[np.concatenate(c.src_tables)])
+        rest = np.setdiff1d(np.arange(64), listed)
+        assert np.all(got[rest] == W.SENTINEL16)
+    # packing with the receiver's ids and unpacking with the same ids reproduces them
+    buf2, _ = o.pack(out, c.dst_tables)
+    assert np.array_equal(buf2, buf)
+
+
+def pin_unpack_out_of_range(o):
+    """Ids past the cache and negative ids are both skipped (a negative id must not wrap
+    around to the last block)."""
+    buf = np.arange(4 * 16, dtype=np.uint8).reshape(1, 4, 16)
+    out, err = o.unpack([buf], [np.zeros((4, 16), np.uint8)], [np.array([3, 7]), np.array([0, -1])])
+    assert err == o.DEVERR_BLOCK_RANGE
+    assert np.array_equal(out[0][3], buf[0, 0]) and np.array_equal(out[0][0], buf[0, 2])
+    assert not out[0][1].any() and not out[0][2].any()
+
+
+def pin_head_merge_golden(o):
+    g = _golden("head_merge_hw6.json")
+    s0 = np.array(g["src0"], np.uint16)
+    s1 = np.array(g["src1"], np.uint16)
+    got = o.unpack_block([s0, s1], g["rows_per_block"]).view(np.uint16).reshape(2, 4)
+    assert got.tolist() == g["expected"]
+
+
+def pin_head_merge_element_loop(o):
+    """Each destination element (token, K/V, head h, dim) comes from sender h // (H/S), local
+    head h % (H/S), at the same buffer position."""
+    for S in (2, 4):
+        H, D, bs, L = 4, 2, 2, 2
+        dspec = W.PagedSpec(L, 10, bs, H, D)
+        rng = np.random.default_rng(S)
+        tables = [np.array([7, 2, 3]), np.array([9])]
+        N = 4
+        bufs = [W.random_words(rng, (L, N, bs, 2, H // S, D)) for _ in range(S)]
+        dst = [np.full(dspec.shape5, W.SENTINEL16, np.uint16) for _ in range(L)]
+        out, err = o.unpack(bufs, dst, tables, rows_per_block=bs * 2)
+        p = 0
+        for r, t in enumerate(tables):
+            for j, blk in enumerate(t):
+                for l in range(L):
+                    got = out[l].view(np.uint16).reshape(dspec.shape5)
+                    for tok in range(bs):
+                        for kv in range(2):
+                            for h in range(H):
+                                for e in range(D):
+                                    s, hl = h // (H // S), h % (H // S)
+                                    assert got[blk, tok, kv, h, e] == bufs[s][l, p, tok, kv, hl, e]
+                p += 1
+
+
+def pin_head_merge_one_source_is_plain(o):
+    c = W.random_transfer(23, 1, 50, 2, 2, 4, [9, 4])
+    buf, _ = o.pack(c.src_caches, c.src_tables)
+    a, _ = o.unpack([buf], c.dst_caches, c.dst_tables, rows_per_block=4)
+    b, _ = o.unpack([buf], c.dst_caches, c.dst_tables, rows_per_block=1)
+    assert np.array_equal(a[0], b[0])
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
