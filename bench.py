@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""KV-cache pack/unpack benchmark on one MI355X.
+
+Workload (the pages' shape): 48 layers, each a separate [147456][16][K,V][128] bf16 cache
+(8 KiB blocks, 1.125 GiB per layer), 8 requests x 576 blocks whose block tables are runs of
+64 consecutive ids; the receiver is a second 48-layer cache with random destination ids.
+All caches are synthetic (seeded random words), resident in HBM before timing starts.
+
+One step = one pass of the whole hot path over that batch:
+  sender:   kvx_build_xfer_list (pack runs) -> kvx_pack (all 48 layers, one launch)
+  receiver: kvx_build_xfer_list (unpack runs) -> kvx_unpack (all 48 layers, one launch)
+            -> kvx_slot_mapping for each request's recomputed last prompt token
+            -> kvx_reshape_and_cache of those 8 tokens into each of the 48 layers
+`value` = algorithmic bytes of the step (read + write of every moved byte) / step time.
+The asymmetric-TP head merge and the 32-request decode write run on their own workloads in
+the same process and are reported under "ops", each with its own roofline.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ops]
+Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "block_table_contiguous_amd", "csrc", f)
+                  for f in ("kvx_kernels.hip", "kvx_launch.h", "kvx_api.hip")]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=["contiguous", "fragmented"], default="contiguous")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ops", action="store_true")
+    ap.add_argument("--op-reps", type=int, default=10)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    return ap.parse_args()
+
+
+class Flush:
+    """Writes a 512 MiB scratch buffer to push earlier data out of the 256 MiB Infinity Cache."""
+
+    def __init__(self, torch, dev):
+        self.t = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def __call__(self):
+        self.t.fill_(0x3C)
+
+
+def time_op(torch, fn, reps, flush):
+    """Median and min kernel time (ms) of fn over reps, with a cache flush before each."""
+    ts = []
+    for _ in range(reps):
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    return ts[len(ts) // 2], ts[0]
+
+
+def copy_calibration(torch, dev):
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}), flush=True)
+
+
+def traffic_from_counters(name: str, launches_bytes: int):
+    """HBM bytes per launch of `name` from the committed rocprofv3 counter summary, scaled by
+    the copy-kernel calibration; None if absent or taken on other kernel sources."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256_16") != kernel_source_hash() or name not in c.get("kernels", {}):
+        return None
+    k = c["kernels"][name]
+    cal = c["copy_calibration"]
+    f_fetch = cal["bytes"] / (cal["FETCH_SIZE_KiB"] * 1024.0)
+    f_write = cal["bytes"] / (cal["WRITE_SIZE_KiB"] * 1024.0)
+    return int(k["FETCH_SIZE_KiB"] * 1024.0 * f_fetch + k["WRITE_SIZE_KiB"] * 1024.0 * f_write)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this path is measured on one GPU only (no second GPU, collective or "
+              "sharded run is part of it); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from block_table_contiguous_amd import kvx as K
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calib:
+        copy_calibration(torch, dev)
+        return
+
+    case = W.pages_contiguous() if args.workload == "contiguous" else W.pages_fragmented()
+    spec = case.src_spec
+    L, nb, BB, N = spec.num_layers, spec.num_blocks, spec.block_bytes, case.total_blocks
+    log(f"workload {case.name}: {L} layers x {nb} blocks x {BB} B, {len(case.src_tables)} requests, N={N}")
+
+    src = [torch.empty((nb, BB), dtype=torch.uint8, device=dev) for _ in range(L)]
+    dst = [torch.empty((nb, BB), dtype=torch.uint8, device=dev) for _ in range(L)]
+    for l in range(L):
+        W.fill_device_random_(src[l], case.seed * 1000 + l)
+        W.fill_device_byte_(dst[l])
+    buf = torch.empty(L * N * BB, dtype=torch.uint8, device=dev)
+    src_bases, dst_bases = K.layer_base_table(src), K.layer_base_table(dst)
+    sid, ro = K.flatten_tables(case.src_tables, dev)
+    did, _ = K.flatten_tables(case.dst_tables, dev)
+    xp, cp = K.new_xfer_list(N, dev)
+    xu, cu = K.new_xfer_list(N, dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    # receiver's recompute of each request's last prompt token (one token per request)
+    R = len(case.dst_tables)
+    row = spec.row_bytes
+    d_table = torch.from_numpy(W.pad_table(case.dst_tables, max(len(t) for t in case.dst_tables))).to(dev)
+    r_idx = torch.arange(R, dtype=torch.int32, device=dev)
+    r_pos = torch.tensor([n - 1 for n in case.lengths], dtype=torch.int64, device=dev)
+    r_slots = torch.empty(R, dtype=torch.int64, device=dev)
+    rng = np.random.default_rng(case.seed + 7)
+    new_k = torch.from_numpy(W.bf16_normal_bits(rng, (L, R, row // 2))).to(dev)
+    new_v = torch.from_numpy(W.bf16_normal_bits(rng, (L, R, row // 2))).to(dev)
+    cnb, cbs, bst, tst, kst = K.cache_strides(
+        dst[0].view(torch.int16).view(nb, spec.block_size, 2, spec.num_kv_heads, spec.head_dim))
+    torch.cuda.synchronize()
+    log("inputs resident")
+
+    ev = {}
+
+    def timed(name, fn, record):
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ev.setdefault(name, []).append((a, b))
+        else:
+            fn()
+
+    def step(record=False):
+        timed("build_pack", lambda: K.kvx_build_xfer_list(sid, None, ro, K.MODE_PACK, xp, cp, err), record)
+        timed("pack", lambda: K.kvx_pack(src_bases, BB, nb, xp, cp, N, buf, err), record)
+        timed("build_unpack", lambda: K.kvx_build_xfer_list(None, did, ro, K.MODE_UNPACK, xu, cu, err), record)
+        timed("unpack", lambda: K.kvx_unpack([buf], dst_bases, BB, nb, 1, xu, cu, N, err), record)
+        K.kvx_slot_mapping(d_table, r_idx, r_pos, spec.block_size, r_slots, err)
+        for l in range(L):
+            K.kvx_reshape_and_cache(new_k[l], new_v[l], r_slots, dst[l], cnb, cbs, bst, tst, kst, err)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, "device error flag raised"
+    log(f"warmup done ({args.warmup} steps)")
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(record=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step")
+
+    copy_bytes = 2 * L * N * BB                    # pack and unpack: each byte read once, written once
+    write_bytes = L * R * (2 * 2 * row + 8)        # new-token write: K,V read+write + slot
+    slot_bytes = R * (4 + 8 + 4 + 8)               # req index, position, table entry, slot
+    step_bytes = 2 * copy_bytes + write_bytes + slot_bytes
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    def avg_ms(name):
+        xs = [a.elapsed_time(b) for a, b in ev[name]]
+        return sum(xs) / len(xs)
+
+    kern = {n: avg_ms(n) for n in ("build_pack", "pack", "build_unpack", "unpack")}
+    dominant = max(("pack", "unpack"), key=lambda n: kern[n])
+    achieved = copy_bytes / (kern[dominant] * 1e-3) / 1e9
+    roofline = {
+        "bound": "hbm", "kernel": f"kvx_{dominant}", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+        "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+        "traffic": traffic_from_counters(f"{dominant}_{case.name}", copy_bytes),
+        "algorithmic_bytes": copy_bytes, "avg_launch_ms": round(kern[dominant], 5),
+    }
+    out_ops = {n: {"avg_ms": round(v, 5)} for n, v in kern.items()}
+    for n in ("pack", "unpack"):
+        out_ops[n]["GB/s"] = round(copy_bytes / (kern[n] * 1e-3) / 1e9, 1)
+        out_ops[n]["frac_of_peak"] = round(copy_bytes / (kern[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    runs_pack, runs_unpack = int(cp.item()), int(cu.item())
+    out_ops["build_pack"]["runs"] = runs_pack
+    out_ops["build_unpack"]["runs"] = runs_unpack
+
+    if not args.no_ops:
+        flush = Flush(torch, dev)
+        med, mn = time_op(torch, lambda: buf[: L * N * BB // 2].copy_(buf[L * N * BB // 2:]), args.op_reps, flush)
+        out_ops["d2d_copy_ceiling"] = {"bytes": L * N * BB, "median_ms": round(med, 5),
+                                       "GB/s": round(L * N * BB / (med * 1e-3) / 1e9, 1)}
+        for n, fn in (("pack", lambda: K.kvx_pack(src_bases, BB, nb, xp, cp, N, buf, err)),
+                      ("unpack", lambda: K.kvx_unpack([buf], dst_bases, BB, nb, 1, xu, cu, N, err))):
+            med, mn = time_op(torch, fn, args.op_reps, flush)
+            out_ops[n]["flushed_median_ms"] = round(med, 5)
+            out_ops[n]["flushed_GB/s"] = round(copy_bytes / (med * 1e-3) / 1e9, 1)
+        out_ops.update(other_workloads(torch, np, W, K, dev, flush, args.op_reps))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(np, W, case, src)
+
+    result = {
+        "metric": "KV pack/unpack effective HBM GB/s (R+W) and % of MI355X peak, 1 GPU",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{case.name}: 48 layers x [147456][16][K,V][128] bf16 (8 KiB blocks), "
+                        f"8 requests x 576 blocks, unpacked to random ids in a second 48-layer cache",
+            "layers": L, "blocks_per_layer": nb, "block_bytes": BB, "requests": R,
+            "blocks_per_request": N // R, "cache_dtype": "bf16", "step_bytes": step_bytes,
+            "parallelism": "single GPU",
+        },
+        "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "ops": out_ops,
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    print(json.dumps(result), flush=True)
+
+
+def other_workloads(torch, np, W, K, dev, flush, reps):
+    """The rows the headline batch does not exercise, each on its own workload."""
+    out = {}
+    # asymmetric-TP receive: 2 sources x 4 heads -> 8-head caches, 32 layers x 4096 blocks
+    case = W.asym_tp()
+    L, N, S = case.dst_spec.num_layers, case.total_blocks, case.num_src
+    BB, nb = case.dst_spec.block_bytes, case.dst_spec.num_blocks
+    srcs = [torch.empty((L, N, BB // S), dtype=torch.uint8, device=dev) for _ in range(S)]
+    for s, t in enumerate(srcs):
+        W.fill_device_random_(t, case.seed * 10 + s)
+    dst = [W.fill_device_byte_(torch.empty((nb, BB), dtype=torch.uint8, device=dev)) for _ in range(L)]
+    bases = K.layer_base_table(dst)
+    ids, ro = K.flatten_tables(case.dst_tables, dev)
+    x, c = K.new_xfer_list(N, dev)
+    K.kvx_build_xfer_list(None, ids, ro, K.MODE_UNPACK, x, c)
+    med, mn = time_op(torch, lambda: K.kvx_unpack(srcs, bases, BB, nb, case.rows_per_block, x, c, N), reps, flush)
+    nbytes = 2 * L * N * BB
+    out["merge_unpack_asym_tp"] = {
+        "workload": "2 sources x 4 of 8 heads, 32 layers x 16 requests x 256 blocks -> [8192][16][K,V][8][128] bf16",
+        "bytes": nbytes, "median_ms": round(med, 4), "min_ms": round(mn, 4),
+        "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del srcs, dst
+    # decode write: 32 requests of 1..2048 tokens into a [4096][16][K,V][8][128] bf16 cache
+    d = W.decode_write()
+    T = len(d.req_idx)
+    bt, rq, pos = (torch.from_numpy(a).to(dev) for a in (d.block_table, d.req_idx, d.positions))
+    slots = torch.empty(T, dtype=torch.int64, device=dev)
+    cache = torch.full(d.spec.shape5, -1, dtype=torch.int16, device=dev)
+    key, val = torch.from_numpy(d.key).to(dev), torch.from_numpy(d.value).to(dev)
+    cnb, cbs, bst, tst, kst = K.cache_strides(cache)
+    med, mn = time_op(torch, lambda: K.kvx_slot_mapping(bt, rq, pos, 16, slots), reps, flush)
+    sbytes = T * (4 + 8 + 4 + 8)
+    out["slot_mapping_decode"] = {"tokens": T, "bytes": sbytes, "median_ms": round(med, 5),
+                                  "GB/s": round(sbytes / (med * 1e-3) / 1e9, 1)}
+    med, mn = time_op(torch, lambda: K.kvx_reshape_and_cache(key, val, slots, cache, cnb, cbs, bst, tst, kst),
+                      reps, flush)
+    wbytes = T * (4 * d.spec.row_bytes + 8)
+    out["reshape_and_cache_decode"] = {
+        "tokens": T, "bytes": wbytes, "median_ms": round(med, 5),
+        "GB/s": round(wbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(wbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    return out
+
+
+def cpu_baseline(np, W, case, src_dev, sample_layers=16):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload: pack and
+    unpack of `sample_layers` of the 48 layers (host copies of the real source layers)."""
+    import oracle as O
+
+    spec = case.src_spec
+    nb, BB = spec.num_blocks, spec.block_bytes
+    step = max(1, spec.num_layers // sample_layers)
+    layers = list(range(0, spec.num_layers, step))[:sample_layers]
+    t_oracle = 0.0
+    for l in layers:
+        src_l = src_dev[l].cpu().numpy()
+        before = np.full((nb, BB), W.FILL_BYTE, np.uint8)
+        t0 = time.perf_counter()
+        buf, _ = O.pack([src_l], case.src_tables)
+        O.unpack([buf], [before], case.dst_tables)
+        t_oracle += time.perf_counter() - t0
+    nbytes = len(layers) * 2 * 2 * case.total_blocks * BB
+    try:
+        cores_avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores_avail = os.cpu_count()
+    return {"value": round(nbytes / t_oracle / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle pack + unpack of {len(layers)} of {spec.num_layers} layers "
+                      f"({nbytes} algorithmic bytes, {t_oracle:.2f} s; numpy, single thread, "
+                      f"{cores_avail} host cores available)"}
+
+
+if __name__ == "__main__":
+    main()

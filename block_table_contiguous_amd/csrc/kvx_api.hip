@@ -1,0 +1,139 @@
+// C-ABI entry points of libkvx: argument validation, then one asynchronous launch each.
+// Validation runs entirely on the host and touches no HIP API, so a bad call returns its
+// status before anything is enqueued (and can be tested without a GPU).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvx.h"
+#include "kvx_launch.h"
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool mult16(int64_t v) { return (v & 15) == 0; }
+
+inline kvx_status from_hip(hipError_t e) { return e == hipSuccess ? KVX_SUCCESS : KVX_ERR_HIP; }
+
+constexpr int64_t kMaxBlocks = 0x7fffffff;  // block ids and run lengths are int32
+
+}  // namespace
+
+extern "C" {
+
+const char* kvx_status_string(kvx_status status) {
+  switch (status) {
+    case KVX_SUCCESS: return "kvx: success";
+    case KVX_ERR_INVALID_ARGUMENT: return "kvx: invalid argument (null pointer, negative size or bad mode)";
+    case KVX_ERR_MISALIGNED: return "kvx: pointer, size or stride not a multiple of 16 bytes";
+    case KVX_ERR_CAPACITY: return "kvx: output array smaller than the worst case";
+    case KVX_ERR_HIP: return "kvx: HIP kernel launch failed";
+  }
+  return "kvx: unknown status";
+}
+
+int32_t kvx_abi_version(void) { return 1; }
+
+kvx_status kvx_slot_mapping(const int32_t* block_table, int64_t num_reqs,
+                            int64_t max_blocks_per_req, int64_t bt_row_stride,
+                            const int32_t* req_idx, const int64_t* positions,
+                            int64_t num_tokens, int32_t block_size, int64_t* slot_mapping,
+                            int32_t* err_flag, hipStream_t stream) {
+  if (num_tokens < 0 || num_reqs < 0 || block_size < 1 || max_blocks_per_req < 0 ||
+      bt_row_stride < max_blocks_per_req)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return KVX_SUCCESS;
+  if (!req_idx || !positions || !slot_mapping || (num_reqs > 0 && !block_table))
+    return KVX_ERR_INVALID_ARGUMENT;
+  return from_hip(kvx::launch_slot_mapping(block_table, num_reqs, max_blocks_per_req,
+                                           bt_row_stride, req_idx, positions, num_tokens,
+                                           block_size, slot_mapping, err_flag, stream));
+}
+
+kvx_status kvx_reshape_and_cache(const void* key, int64_t key_stride_bytes, const void* value,
+                                 int64_t value_stride_bytes, int64_t num_tokens,
+                                 int64_t row_bytes, const int64_t* slot_mapping,
+                                 void* kv_cache, int64_t num_blocks, int32_t block_size,
+                                 int64_t block_stride_bytes, int64_t token_stride_bytes,
+                                 int64_t kv_stride_bytes, int32_t* err_flag,
+                                 hipStream_t stream) {
+  if (num_tokens < 0 || row_bytes <= 0 || num_blocks < 0 || block_size < 1 ||
+      key_stride_bytes < 0 || value_stride_bytes < 0 || block_stride_bytes < 0 ||
+      token_stride_bytes < 0 || kv_stride_bytes < 0)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return KVX_SUCCESS;
+  if (!key || !value || !slot_mapping || !kv_cache) return KVX_ERR_INVALID_ARGUMENT;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(kv_cache) || !mult16(row_bytes) ||
+      !mult16(key_stride_bytes) || !mult16(value_stride_bytes) || !mult16(block_stride_bytes) ||
+      !mult16(token_stride_bytes) || !mult16(kv_stride_bytes))
+    return KVX_ERR_MISALIGNED;
+  return from_hip(kvx::launch_reshape_and_cache(
+      key, key_stride_bytes, value, value_stride_bytes, num_tokens, row_bytes, slot_mapping,
+      kv_cache, num_blocks, block_size, block_stride_bytes, token_stride_bytes, kv_stride_bytes,
+      err_flag, stream));
+}
+
+kvx_status kvx_build_xfer_list(const int32_t* src_ids, const int32_t* dst_ids,
+                               const int64_t* req_offsets, int32_t num_reqs,
+                               int64_t total_blocks, int32_t mode, kvx_xfer* xfers,
+                               int64_t capacity, int64_t* xfer_count, int32_t* err_flag,
+                               hipStream_t stream) {
+  if (mode != KVX_MODE_PACK && mode != KVX_MODE_UNPACK && mode != KVX_MODE_DIRECT)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (num_reqs < 0 || total_blocks < 0 || total_blocks > kMaxBlocks || capacity < 0)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (!xfer_count || !req_offsets) return KVX_ERR_INVALID_ARGUMENT;
+  if (total_blocks > 0 && num_reqs == 0) return KVX_ERR_INVALID_ARGUMENT;
+  if (total_blocks > 0) {
+    const bool need_src = mode != KVX_MODE_UNPACK, need_dst = mode != KVX_MODE_PACK;
+    if ((need_src && !src_ids) || (need_dst && !dst_ids) || !xfers) return KVX_ERR_INVALID_ARGUMENT;
+  }
+  if (((uintptr_t)xfers & 7u) != 0) return KVX_ERR_MISALIGNED;
+  if (capacity < total_blocks) return KVX_ERR_CAPACITY;
+  return from_hip(kvx::launch_build_xfer_list(src_ids, dst_ids, req_offsets, num_reqs,
+                                              total_blocks, mode, xfers, xfer_count, err_flag,
+                                              stream));
+}
+
+kvx_status kvx_pack(void* const* layer_bases, int32_t num_layers, int64_t block_bytes,
+                    int64_t num_cache_blocks, const kvx_xfer* xfers,
+                    const int64_t* xfer_count, int64_t total_blocks, void* send_buf,
+                    int32_t* err_flag, hipStream_t stream) {
+  if (num_layers < 0 || block_bytes <= 0 || num_cache_blocks < 0 || total_blocks < 0 ||
+      total_blocks > kMaxBlocks)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (num_layers == 0 || total_blocks == 0) return KVX_SUCCESS;
+  if (!layer_bases || !xfers || !xfer_count || !send_buf) return KVX_ERR_INVALID_ARGUMENT;
+  if (!mult16(block_bytes) || !aligned16(send_buf)) return KVX_ERR_MISALIGNED;
+  return from_hip(kvx::launch_copy_runs(true, layer_bases, num_layers, block_bytes,
+                                        num_cache_blocks, xfers, xfer_count, total_blocks,
+                                        send_buf, err_flag, stream));
+}
+
+kvx_status kvx_unpack(const void* const* send_bufs, int32_t num_src, void* const* layer_bases,
+                      int32_t num_layers, int64_t block_bytes, int64_t num_cache_blocks,
+                      int32_t rows_per_block, const kvx_xfer* xfers,
+                      const int64_t* xfer_count, int64_t total_blocks, int32_t* err_flag,
+                      hipStream_t stream) {
+  if (num_src < 1 || num_src > KVX_MAX_SOURCES || num_layers < 0 || block_bytes <= 0 ||
+      num_cache_blocks < 0 || total_blocks < 0 || total_blocks > kMaxBlocks ||
+      rows_per_block < 1)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (!mult16(block_bytes)) return KVX_ERR_MISALIGNED;
+  if (num_src > 1 && block_bytes % ((int64_t)rows_per_block * num_src * 16) != 0)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (num_layers == 0 || total_blocks == 0) return KVX_SUCCESS;
+  if (!send_bufs || !layer_bases || !xfers || !xfer_count) return KVX_ERR_INVALID_ARGUMENT;
+  for (int32_t s = 0; s < num_src; ++s) {
+    if (!send_bufs[s]) return KVX_ERR_INVALID_ARGUMENT;
+    if (!aligned16(send_bufs[s])) return KVX_ERR_MISALIGNED;
+  }
+  if (num_src == 1)
+    return from_hip(kvx::launch_copy_runs(false, layer_bases, num_layers, block_bytes,
+                                          num_cache_blocks, xfers, xfer_count, total_blocks,
+                                          const_cast<void*>(send_bufs[0]), err_flag, stream));
+  return from_hip(kvx::launch_merge_runs(send_bufs, num_src, layer_bases, num_layers, block_bytes,
+                                         num_cache_blocks, rows_per_block, xfers, xfer_count,
+                                         total_blocks, err_flag, stream));
+}
+
+}  // extern "C"

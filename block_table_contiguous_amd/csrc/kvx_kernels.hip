@@ -1,0 +1,640 @@
+// gfx950 (CDNA4) kernels for the paged KV-cache transfer path.
+//
+// Everything here is pure data movement: no floating-point arithmetic, no MFMA. Bytes move
+// as 16-byte vectors through VGPRs (global_load_dwordx4 / global_store_dwordx4); a
+// wavefront's 64 lanes cover 1 KiB of consecutive bytes per instruction, so every access is
+// fully coalesced, and each lane keeps several loads in flight before it stores.
+//
+// Sources: slot rule of the batch-tensor label and the 16-slot block of the "Paged kv cache"
+// label ("vllm v1 调度逻辑 和 distributed 分布式原理"); transfer-list flattening of
+// "5. flagcx connector design & dev & test" §1.2 (_send_blocks); per-layer base + block
+// length x id addressing of "vLLM PD 分离" §七 item 3; TP heterogeneity of §四 4.2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "kvx.h"
+#include "kvx_launch.h"
+
+namespace kvx {
+
+// --------------------------------------------------------------------------------------
+// tuning knobs
+// --------------------------------------------------------------------------------------
+
+static int64_t env_i64(const char* name, int64_t dflt) {
+  const char* s = getenv(name);
+  if (!s || !*s) return dflt;
+  char* end = nullptr;
+  long long v = strtoll(s, &end, 0);
+  return (end && *end == '\0') ? (int64_t)v : dflt;
+}
+
+const Tuning& tuning() {
+  static const Tuning t = {
+      env_i64("KVX_WAVE_BYTES", 64 * 1024),
+      (int)env_i64("KVX_XCD_REMAP", 1),
+      (int)env_i64("KVX_NT", 0),
+  };
+  return t;
+}
+
+// --------------------------------------------------------------------------------------
+// device helpers
+// --------------------------------------------------------------------------------------
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#define KVX_GLOBAL __attribute__((address_space(1)))
+
+constexpr int kWave = 64;
+constexpr int kVec = 16;                 // bytes per lane access
+constexpr int kWaveBytes = kWave * kVec; // bytes per wavefront instruction
+constexpr int kNumXcd = 8;               // MI355X: 8 XCDs, workgroups dealt round-robin
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const char* p) {
+  const KVX_GLOBAL u32x4* g = (const KVX_GLOBAL u32x4*)p;
+  if constexpr (NT) return __builtin_nontemporal_load(g);
+  else return *g;
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(char* p, u32x4 v) {
+  KVX_GLOBAL u32x4* g = (KVX_GLOBAL u32x4*)p;
+  if constexpr (NT) __builtin_nontemporal_store(v, g);
+  else *g = v;
+}
+
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const int32_t lo = __builtin_amdgcn_readfirstlane((int32_t)(v & 0xffffffff));
+  const int32_t hi = __builtin_amdgcn_readfirstlane((int32_t)(v >> 32));
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+__device__ __forceinline__ void raise_error(int32_t* err, int32_t bit) {
+  if (err) atomicOr(err, bit);
+}
+
+// Workgroup b runs on XCD b % 8. Renumber so that XCD x owns one contiguous slice of the
+// workgroup index space: each XCD's L2 and address-translation caches then see 1/8 of the
+// layers instead of all of them.
+__device__ __forceinline__ int64_t xcd_slice_order(int64_t b, int64_t n) {
+  const int64_t xcd = b % kNumXcd, idx = b / kNumXcd;
+  const int64_t per = n / kNumXcd, rem = n % kNumXcd;
+  return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+// One wavefront copies nbytes (a multiple of 16) from src to dst. Batch j of K covers
+// bytes [base + j KiB, base + (j+1) KiB): each instruction is one coalesced 1 KiB access,
+// and a lane issues all K loads of a batch before its K stores.
+template <int K, bool NTL, bool NTS>
+__device__ __forceinline__ void wave_copy(const char* __restrict__ src, char* __restrict__ dst,
+                                          int64_t nbytes, int lane) {
+  constexpr int64_t kBatch = (int64_t)K * kWaveBytes;
+  const int64_t lo = (int64_t)lane * kVec;
+  int64_t base = 0;
+  for (; base + kBatch <= nbytes; base += kBatch) {
+    u32x4 v[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) v[j] = load16<NTL>(src + base + j * kWaveBytes + lo);
+#pragma unroll
+    for (int j = 0; j < K; ++j) store16<NTS>(dst + base + j * kWaveBytes + lo, v[j]);
+  }
+  if (base < nbytes) {
+    u32x4 v[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t o = base + j * kWaveBytes + lo;
+      if (o < nbytes) v[j] = load16<NTL>(src + o);
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t o = base + j * kWaveBytes + lo;
+      if (o < nbytes) store16<NTS>(dst + o, v[j]);
+    }
+  }
+}
+
+// Index of the last run whose buf_block <= p (runs sorted by buf_block), or -1. A 64-way
+// search: every lane probes one pivot, a ballot picks the bracket; <= 3 rounds for 2^18 runs.
+__device__ __forceinline__ int64_t find_run(const kvx_xfer* __restrict__ xfers, int64_t count,
+                                            int64_t p, int lane) {
+  int64_t lo = 0, hi = count;  // answer in [lo - 1, hi)
+  while (hi - lo > 1) {
+    const int64_t step = (hi - lo + kWave - 1) / kWave;
+    const int64_t idx = lo + (int64_t)lane * step;
+    const bool pred = idx < hi && xfers[idx].buf_block <= p;
+    const uint64_t m = __ballot(pred);
+    if (m == 0) return lo - 1;
+    const int64_t j = 63 - __builtin_clzll(m);
+    lo = lo + j * step;
+    hi = (lo + step < hi) ? lo + step : hi;
+  }
+  if (hi - lo == 1 && xfers[lo].buf_block > p) return lo - 1;
+  return lo;
+}
+
+// --------------------------------------------------------------------------------------
+// a1 — slot mapping: one thread per token
+// --------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    const int32_t* __restrict__ block_table, int64_t num_reqs, int64_t max_cols,
+    int64_t row_stride, const int32_t* __restrict__ req_idx,
+    const int64_t* __restrict__ positions, int64_t num_tokens, int32_t block_size,
+    int64_t* __restrict__ slots, int32_t* err) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < num_tokens; i += stride) {
+    const int64_t r = req_idx[i];
+    const int64_t pos = positions[i];
+    int64_t slot = -1;
+    if (r >= 0 && r < num_reqs && pos >= 0) {
+      int64_t col, off;
+      if (pos <= 0x7fffffff) {  // 32-bit division for every realistic position
+        col = (uint32_t)pos / (uint32_t)block_size;
+        off = (uint32_t)pos - (uint32_t)col * (uint32_t)block_size;
+      } else {
+        col = pos / block_size;
+        off = pos - col * block_size;
+      }
+      if (col < max_cols) {
+        const int32_t b = block_table[r * row_stride + col];
+        if (b >= 0) slot = (int64_t)b * block_size + off;
+      }
+    }
+    slots[i] = slot;
+    if (slot < 0) raise_error(err, KVX_DEVERR_TABLE_RANGE);
+  }
+}
+
+// --------------------------------------------------------------------------------------
+// a2 — new-token K/V write: one wavefront per token, K row and V row in one pass
+// --------------------------------------------------------------------------------------
+
+template <int K>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const char* __restrict__ key, int64_t key_stride, const char* __restrict__ value,
+    int64_t value_stride, int64_t num_tokens, int64_t row_bytes,
+    const int64_t* __restrict__ slots, char* __restrict__ cache, int64_t num_blocks,
+    int32_t block_size, int64_t block_stride, int64_t token_stride, int64_t kv_stride,
+    int32_t* err) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t waves_per_wg = blockDim.x / kWave;
+  const int64_t wave = uniform((int64_t)blockIdx.x * waves_per_wg + (threadIdx.x / kWave));
+  const int64_t num_waves = (int64_t)gridDim.x * waves_per_wg;
+  const int64_t nvec = row_bytes / kVec;  // vectors in one row
+  for (int64_t t = wave; t < num_tokens; t += num_waves) {
+    const int64_t s = uniform(slots[t]);
+    if (s < 0) continue;  // padding token
+    int64_t blk, off;
+    if (s <= 0x7fffffff) {
+      blk = (uint32_t)s / (uint32_t)block_size;
+      off = (uint32_t)s - (uint32_t)blk * (uint32_t)block_size;
+    } else {
+      blk = s / block_size;
+      off = s - blk * block_size;
+    }
+    if (blk >= num_blocks) {
+      if (lane == 0) raise_error(err, KVX_DEVERR_SLOT_RANGE);
+      continue;
+    }
+    char* base = cache + blk * block_stride + off * token_stride;
+    const char* krow = key + t * key_stride;
+    const char* vrow = value + t * value_stride;
+    // vectors q in [0, 2*nvec): q < nvec -> K row, else V row
+    for (int64_t q0 = 0; q0 < 2 * nvec; q0 += (int64_t)K * kWave) {
+      u32x4 v[K];
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int64_t q = q0 + j * kWave + lane;
+        if (q < 2 * nvec) v[j] = load16<false>(q < nvec ? krow + q * kVec : vrow + (q - nvec) * kVec);
+      }
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int64_t q = q0 + j * kWave + lane;
+        if (q < 2 * nvec)
+          store16<false>(q < nvec ? base + q * kVec : base + kv_stride + (q - nvec) * kVec, v[j]);
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------------------
+// a3 — transfer list: run-start flags -> workgroup prefix scan -> compaction
+// --------------------------------------------------------------------------------------
+
+constexpr int kScanThreads = 1024;
+constexpr int kScanItems = 4;
+constexpr int kScanTile = kScanThreads * kScanItems;
+constexpr int kScanWaves = kScanThreads / kWave;
+
+// Largest r in [0, R) with req_offsets[r] <= p (0 if none).
+__device__ __forceinline__ int32_t find_request(const int64_t* __restrict__ ro, int32_t R, int64_t p) {
+  int32_t lo = 0, hi = R - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (ro[mid] <= p) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Single workgroup of 1024 threads walks the blocks in tiles of 4096. Per tile: every thread
+// flags run starts among its 4 consecutive positions, a wave scan (DPP shuffles) plus a
+// 16-entry LDS pass turns the flags into run indices, and each thread writes the runs it
+// starts and the lengths of the runs it ends. The scan carries two quantities: the number of
+// starts so far (the run index) and the position of the latest start (for run lengths).
+__global__ __launch_bounds__(kScanThreads) void build_xfer_kernel(
+    const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
+    const int64_t* __restrict__ ro, int32_t R, int64_t N, int32_t mode,
+    kvx_xfer* __restrict__ out, int64_t* __restrict__ count, int32_t* err) {
+  __shared__ int64_t s_cnt[kScanWaves];
+  __shared__ int64_t s_last[kScanWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  const bool use_src = mode != KVX_MODE_UNPACK;
+  const bool use_dst = mode != KVX_MODE_PACK;
+
+  // CSR sanity: ro[0] == 0, non-decreasing, ro[R] == N
+  for (int32_t i = tid; i < R; i += kScanThreads)
+    if (ro[i + 1] < ro[i]) raise_error(err, KVX_DEVERR_OFFSETS);
+  if (tid == 0 && (ro[0] != 0 || ro[R] != N)) raise_error(err, KVX_DEVERR_OFFSETS);
+
+  int64_t carry_cnt = 0, carry_last = -1;
+  for (int64_t tile = 0; tile < N; tile += kScanTile) {
+    const int64_t p0 = tile + (int64_t)tid * kScanItems;
+    // ids at p0-1 .. p0+kScanItems (one before for the step test, one after for run ends)
+    int64_t sv[kScanItems + 2], dv[kScanItems + 2];
+#pragma unroll
+    for (int i = 0; i < kScanItems + 2; ++i) {
+      const int64_t p = p0 - 1 + i;
+      const bool in = p >= 0 && p < N;
+      sv[i] = (use_src && in) ? (int64_t)src[p] : 0;
+      dv[i] = (use_dst && in) ? (int64_t)dst[p] : 0;
+    }
+    int32_t r = (p0 < N) ? find_request(ro, R, p0) : 0;
+    bool st[kScanItems + 1];
+    int32_t rq[kScanItems];
+    int64_t cnt = 0, last = -1;
+#pragma unroll
+    for (int i = 0; i <= kScanItems; ++i) {
+      const int64_t p = p0 + i;
+      bool s = false;
+      if (p < N) {
+        while (r + 1 < R && ro[r + 1] <= p) ++r;
+        s = (p == 0) || (p == ro[r]) || (use_src && sv[i + 1] != sv[i] + 1) ||
+            (use_dst && dv[i + 1] != dv[i] + 1);
+      }
+      st[i] = s;
+      if (i < kScanItems) {
+        rq[i] = r;
+        if (s) { ++cnt; last = p; }
+      }
+    }
+
+    // workgroup scan of (cnt: sum, last: max)
+    int64_t ci = cnt, li = last;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int64_t c = __shfl_up(ci, d, kWave);
+      const int64_t l = __shfl_up(li, d, kWave);
+      if (lane >= d) { ci += c; li = l > li ? l : li; }
+    }
+    int64_t li_excl = __shfl_up(li, 1, kWave);
+    if (lane == 0) li_excl = -1;
+    if (lane == kWave - 1) { s_cnt[wid] = ci; s_last[wid] = li; }
+    __syncthreads();
+    int64_t c_before = 0, l_before = -1, c_tile = 0, l_tile = -1;
+#pragma unroll
+    for (int w = 0; w < kScanWaves; ++w) {
+      const int64_t c = s_cnt[w], l = s_last[w];
+      if (w < wid) { c_before += c; l_before = l > l_before ? l : l_before; }
+      c_tile += c;
+      l_tile = l > l_tile ? l : l_tile;
+    }
+    __syncthreads();
+
+    int64_t k = carry_cnt + c_before + (ci - cnt);
+    int64_t cur = carry_last;
+    if (l_before > cur) cur = l_before;
+    if (li_excl > cur) cur = li_excl;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+      const int64_t p = p0 + i;
+      if (p < N) {
+        if (st[i]) {
+          kvx_xfer* x = out + k;
+          x->src_block = use_src ? sv[i + 1] : p;
+          x->dst_block = use_dst ? dv[i + 1] : p;
+          x->buf_block = p;
+          x->req = rq[i];
+          cur = p;
+          ++k;
+        }
+        if (p == N - 1 || st[i + 1]) out[k - 1].num_blocks = (int32_t)(p - cur + 1);
+      }
+    }
+    carry_cnt += c_tile;
+    if (l_tile > carry_last) carry_last = l_tile;
+  }
+  if (tid == 0) *count = carry_cnt;
+}
+
+// --------------------------------------------------------------------------------------
+// a4 / a5 — pack and single-source unpack over the run list
+// --------------------------------------------------------------------------------------
+
+struct RunCopyArgs {
+  const char* const* layer_bases;
+  char* buffer;
+  const kvx_xfer* xfers;
+  const int64_t* xfer_count;
+  int32_t* err;
+  int64_t block_bytes;
+  int64_t num_cache_blocks;
+  int64_t total_blocks;
+  int64_t blocks_per_wave;
+  int64_t waves_per_layer;
+  int64_t total_waves;
+  int64_t num_wgs;
+  int32_t num_layers;
+  int32_t xcd_remap;
+};
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyWavesPerWg = kCopyThreads / kWave;
+constexpr int kCopyBatch = 8;  // 1 KiB loads in flight per lane batch = 8 KiB per wavefront
+
+// Work split: wavefront w owns layer l = w / waves_per_layer and buffer positions
+// [c*B, min((c+1)*B, N)) of that layer (B = blocks_per_wave), so every wavefront moves the
+// same number of bytes whatever the run lengths. It finds the run holding its first
+// position, then walks the runs overlapping its range; each overlap is one contiguous copy
+// on both sides (run blocks are consecutive in the cache and in the buffer).
+template <bool TO_BUFFER, bool NTL, bool NTS>
+__global__ __launch_bounds__(kCopyThreads) void copy_runs_kernel(RunCopyArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t wg = blockIdx.x;
+  if (a.xcd_remap) wg = xcd_slice_order(wg, a.num_wgs);
+  const int64_t w = uniform(wg * kCopyWavesPerWg + (threadIdx.x / kWave));
+  if (w >= a.total_waves) return;
+  const int64_t l = w / a.waves_per_layer;
+  const int64_t c = w - l * a.waves_per_layer;
+  const int64_t N = a.total_blocks;
+  const int64_t p0 = c * a.blocks_per_wave;
+  const int64_t p1 = (p0 + a.blocks_per_wave < N) ? p0 + a.blocks_per_wave : N;
+  const int64_t BB = a.block_bytes;
+  int64_t count = *a.xfer_count;
+  if (count > N) count = N;
+  if (count <= 0) return;
+  char* cache = const_cast<char*>(a.layer_bases[l]);
+  char* buf = a.buffer + l * N * BB;
+
+  int64_t k = uniform(find_run(a.xfers, count, p0, lane));
+  if (k < 0) k = 0;
+  bool bad = false;
+  for (; k < count; ++k) {
+    const kvx_xfer x = a.xfers[k];
+    const int64_t rb = x.buf_block;
+    if (rb >= p1) break;
+    const int64_t lo = rb > p0 ? rb : p0;
+    const int64_t re = rb + (int64_t)x.num_blocks;
+    const int64_t hi = re < p1 ? re : p1;
+    if (lo >= hi) continue;
+    const int64_t id0 = (TO_BUFFER ? x.src_block : x.dst_block) + (lo - rb);
+    const int64_t id1 = id0 + (hi - lo);
+    const int64_t v0 = id0 > 0 ? id0 : 0;
+    const int64_t v1 = id1 < a.num_cache_blocks ? id1 : a.num_cache_blocks;
+    if (v0 != id0 || v1 != id1) bad = true;
+    if (v0 >= v1) continue;
+    char* cptr = cache + v0 * BB;
+    char* bptr = buf + (lo + (v0 - id0)) * BB;
+    if (TO_BUFFER) wave_copy<kCopyBatch, NTL, NTS>(cptr, bptr, (v1 - v0) * BB, lane);
+    else wave_copy<kCopyBatch, NTL, NTS>(bptr, cptr, (v1 - v0) * BB, lane);
+  }
+  if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_BLOCK_RANGE);
+}
+
+// --------------------------------------------------------------------------------------
+// a6 — unpack merging head-split sources
+// --------------------------------------------------------------------------------------
+
+struct MergeArgs {
+  const char* src[KVX_MAX_SOURCES];
+  const char* const* layer_bases;
+  const kvx_xfer* xfers;
+  const int64_t* xfer_count;
+  int32_t* err;
+  int64_t block_bytes;       // destination block
+  int64_t num_cache_blocks;
+  int64_t total_blocks;
+  int64_t row_src;           // bytes of one source row
+  int64_t blocks_per_wave;
+  int64_t waves_per_layer;
+  int64_t total_waves;
+  int64_t num_wgs;
+  int32_t num_src;
+  int32_t rows_per_block;
+  int32_t num_layers;
+  int32_t xcd_remap;
+};
+
+// Same work split as copy_runs_kernel. For each overlap of n blocks the destination is
+// n*rows_per_block rows of num_src*row_src bytes; source s supplies the s-th row_src piece of
+// every row from its own contiguous n*rows_per_block*row_src bytes. Per source the wavefront
+// streams the source rows in order (one 1 KiB instruction per row piece when row_src is
+// 1 KiB) and writes them at the destination row stride.
+template <bool NTL, bool NTS>
+__global__ __launch_bounds__(kCopyThreads) void merge_runs_kernel(MergeArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t wg = blockIdx.x;
+  if (a.xcd_remap) wg = xcd_slice_order(wg, a.num_wgs);
+  const int64_t w = uniform(wg * kCopyWavesPerWg + (threadIdx.x / kWave));
+  if (w >= a.total_waves) return;
+  const int64_t l = w / a.waves_per_layer;
+  const int64_t c = w - l * a.waves_per_layer;
+  const int64_t N = a.total_blocks;
+  const int64_t p0 = c * a.blocks_per_wave;
+  const int64_t p1 = (p0 + a.blocks_per_wave < N) ? p0 + a.blocks_per_wave : N;
+  const int64_t S = a.num_src;
+  const int64_t BB = a.block_bytes;
+  const int64_t BBs = BB / S;
+  const int64_t row_src = a.row_src;
+  const int64_t row_dst = row_src * S;
+  const int64_t vs = row_src / kVec;                  // vectors per source row
+  const int64_t M = (vs + kWave - 1) / kWave;         // instructions per source row
+  int64_t count = *a.xfer_count;
+  if (count > N) count = N;
+  if (count <= 0) return;
+  char* cache = const_cast<char*>(a.layer_bases[l]);
+
+  int64_t k = uniform(find_run(a.xfers, count, p0, lane));
+  if (k < 0) k = 0;
+  bool bad = false;
+  for (; k < count; ++k) {
+    const kvx_xfer x = a.xfers[k];
+    const int64_t rb = x.buf_block;
+    if (rb >= p1) break;
+    const int64_t lo = rb > p0 ? rb : p0;
+    const int64_t re = rb + (int64_t)x.num_blocks;
+    const int64_t hi = re < p1 ? re : p1;
+    if (lo >= hi) continue;
+    const int64_t id0 = x.dst_block + (lo - rb);
+    const int64_t id1 = id0 + (hi - lo);
+    const int64_t v0 = id0 > 0 ? id0 : 0;
+    const int64_t v1 = id1 < a.num_cache_blocks ? id1 : a.num_cache_blocks;
+    if (v0 != id0 || v1 != id1) bad = true;
+    if (v0 >= v1) continue;
+    const int64_t bpos = lo + (v0 - id0);
+    char* dblk = cache + v0 * BB;
+    const int64_t rows = (v1 - v0) * a.rows_per_block;
+    const int64_t steps = rows * M;
+    for (int64_t s = 0; s < S; ++s) {
+      const char* sblk = a.src[s] + (l * N + bpos) * BBs;
+      char* dcol = dblk + s * row_src;
+      int64_t row = 0, m = 0;
+      for (int64_t t0 = 0; t0 < steps; t0 += kCopyBatch) {
+        const char* sp[kCopyBatch];
+        char* dp[kCopyBatch];
+        bool act[kCopyBatch];
+#pragma unroll
+        for (int j = 0; j < kCopyBatch; ++j) {
+          const int64_t xv = m * kWave + lane;
+          act[j] = (t0 + j < steps) && (xv < vs);
+          sp[j] = sblk + row * row_src + xv * kVec;
+          dp[j] = dcol + row * row_dst + xv * kVec;
+          if (++m == M) { m = 0; ++row; }
+        }
+        u32x4 v[kCopyBatch];
+#pragma unroll
+        for (int j = 0; j < kCopyBatch; ++j)
+          if (act[j]) v[j] = load16<NTL>(sp[j]);
+#pragma unroll
+        for (int j = 0; j < kCopyBatch; ++j)
+          if (act[j]) store16<NTS>(dp[j], v[j]);
+      }
+    }
+  }
+  if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_BLOCK_RANGE);
+}
+
+// --------------------------------------------------------------------------------------
+// launchers
+// --------------------------------------------------------------------------------------
+
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+hipError_t launch_slot_mapping(const int32_t* block_table, int64_t num_reqs, int64_t max_cols,
+                               int64_t row_stride, const int32_t* req_idx,
+                               const int64_t* positions, int64_t num_tokens, int32_t block_size,
+                               int64_t* slots, int32_t* err, hipStream_t stream) {
+  const int64_t wgs = ceil_div(num_tokens, 256);
+  const unsigned grid = (unsigned)(wgs < (1 << 20) ? wgs : (1 << 20));
+  slot_mapping_kernel<<<grid, 256, 0, stream>>>(block_table, num_reqs, max_cols, row_stride,
+                                                req_idx, positions, num_tokens, block_size,
+                                                slots, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache(const void* key, int64_t key_stride, const void* value,
+                                    int64_t value_stride, int64_t num_tokens, int64_t row_bytes,
+                                    const int64_t* slots, void* cache, int64_t num_blocks,
+                                    int32_t block_size, int64_t block_stride,
+                                    int64_t token_stride, int64_t kv_stride, int32_t* err,
+                                    hipStream_t stream) {
+  const int64_t wgs = ceil_div(num_tokens, 4);
+  const unsigned grid = (unsigned)(wgs < (1 << 20) ? wgs : (1 << 20));
+  reshape_and_cache_kernel<4><<<grid, 256, 0, stream>>>(
+      (const char*)key, key_stride, (const char*)value, value_stride, num_tokens, row_bytes,
+      slots, (char*)cache, num_blocks, block_size, block_stride, token_stride, kv_stride, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_xfer_list(const int32_t* src_ids, const int32_t* dst_ids,
+                                  const int64_t* req_offsets, int32_t num_reqs,
+                                  int64_t total_blocks, int32_t mode, kvx_xfer* xfers,
+                                  int64_t* xfer_count, int32_t* err, hipStream_t stream) {
+  build_xfer_kernel<<<1, kScanThreads, 0, stream>>>(src_ids, dst_ids, req_offsets, num_reqs,
+                                                    total_blocks, mode, xfers, xfer_count, err);
+  return hipGetLastError();
+}
+
+// Blocks per wavefront: about wave_bytes of buffer each, and few enough wavefronts that the
+// grid stays well inside 32-bit workgroup counts.
+static int64_t blocks_per_wave_for(int64_t block_bytes, int64_t num_layers, int64_t N) {
+  int64_t bpw = tuning().wave_bytes / block_bytes;
+  if (bpw < 1) bpw = 1;
+  const int64_t max_waves = (int64_t)1 << 30;
+  const int64_t min_bpw = ceil_div(num_layers * N, max_waves);
+  return bpw > min_bpw ? bpw : min_bpw;
+}
+
+template <bool TO_BUFFER>
+static void launch_copy_variant(const RunCopyArgs& a, unsigned grid, hipStream_t stream) {
+  switch (tuning().nt_mode & 3) {
+    case 0: copy_runs_kernel<TO_BUFFER, false, false><<<grid, kCopyThreads, 0, stream>>>(a); break;
+    case 1: copy_runs_kernel<TO_BUFFER, true, false><<<grid, kCopyThreads, 0, stream>>>(a); break;
+    case 2: copy_runs_kernel<TO_BUFFER, false, true><<<grid, kCopyThreads, 0, stream>>>(a); break;
+    default: copy_runs_kernel<TO_BUFFER, true, true><<<grid, kCopyThreads, 0, stream>>>(a); break;
+  }
+}
+
+hipError_t launch_copy_runs(bool to_buffer, void* const* layer_bases, int32_t num_layers,
+                            int64_t block_bytes, int64_t num_cache_blocks, const kvx_xfer* xfers,
+                            const int64_t* xfer_count, int64_t total_blocks, void* buffer,
+                            int32_t* err, hipStream_t stream) {
+  RunCopyArgs a;
+  a.layer_bases = (const char* const*)layer_bases;
+  a.buffer = (char*)buffer;
+  a.xfers = xfers;
+  a.xfer_count = xfer_count;
+  a.err = err;
+  a.block_bytes = block_bytes;
+  a.num_cache_blocks = num_cache_blocks;
+  a.total_blocks = total_blocks;
+  a.blocks_per_wave = blocks_per_wave_for(block_bytes, num_layers, total_blocks);
+  a.waves_per_layer = ceil_div(total_blocks, a.blocks_per_wave);
+  a.total_waves = a.waves_per_layer * num_layers;
+  a.num_wgs = ceil_div(a.total_waves, kCopyWavesPerWg);
+  a.num_layers = num_layers;
+  a.xcd_remap = tuning().xcd_remap;
+  const unsigned grid = (unsigned)a.num_wgs;
+  if (to_buffer) launch_copy_variant<true>(a, grid, stream);
+  else launch_copy_variant<false>(a, grid, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_runs(const void* const* srcs, int32_t num_src, void* const* layer_bases,
+                             int32_t num_layers, int64_t block_bytes, int64_t num_cache_blocks,
+                             int32_t rows_per_block, const kvx_xfer* xfers,
+                             const int64_t* xfer_count, int64_t total_blocks, int32_t* err,
+                             hipStream_t stream) {
+  MergeArgs a;
+  for (int i = 0; i < KVX_MAX_SOURCES; ++i) a.src[i] = i < num_src ? (const char*)srcs[i] : nullptr;
+  a.layer_bases = (const char* const*)layer_bases;
+  a.xfers = xfers;
+  a.xfer_count = xfer_count;
+  a.err = err;
+  a.block_bytes = block_bytes;
+  a.num_cache_blocks = num_cache_blocks;
+  a.total_blocks = total_blocks;
+  a.row_src = block_bytes / ((int64_t)rows_per_block * num_src);
+  a.blocks_per_wave = blocks_per_wave_for(block_bytes, num_layers, total_blocks);
+  a.waves_per_layer = ceil_div(total_blocks, a.blocks_per_wave);
+  a.total_waves = a.waves_per_layer * num_layers;
+  a.num_wgs = ceil_div(a.total_waves, kCopyWavesPerWg);
+  a.num_src = num_src;
+  a.rows_per_block = rows_per_block;
+  a.num_layers = num_layers;
+  a.xcd_remap = tuning().xcd_remap;
+  const unsigned grid = (unsigned)a.num_wgs;
+  switch (tuning().nt_mode & 3) {
+    case 0: merge_runs_kernel<false, false><<<grid, kCopyThreads, 0, stream>>>(a); break;
+    case 1: merge_runs_kernel<true, false><<<grid, kCopyThreads, 0, stream>>>(a); break;
+    case 2: merge_runs_kernel<false, true><<<grid, kCopyThreads, 0, stream>>>(a); break;
+    default: merge_runs_kernel<true, true><<<grid, kCopyThreads, 0, stream>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvx

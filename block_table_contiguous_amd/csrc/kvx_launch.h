@@ -1,0 +1,51 @@
+// Internal interface between the C-ABI entry points (kvx_api.hip) and the gfx950 kernels
+// (kvx_kernels.hip). Arguments are already validated when these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvx.h"
+
+namespace kvx {
+
+// Launch-shape knobs. Defaults are compiled in; each can be overridden once per process
+// through the environment (read on first use) so sweeps need no rebuild.
+struct Tuning {
+  int64_t wave_bytes;  // bytes of buffer one wavefront owns in pack/unpack (KVX_WAVE_BYTES)
+  int xcd_remap;       // 1: give each XCD a contiguous slice of the work (KVX_XCD_REMAP)
+  int nt_mode;         // bit 0: non-temporal loads, bit 1: non-temporal stores (KVX_NT)
+};
+const Tuning& tuning();
+
+hipError_t launch_slot_mapping(const int32_t* block_table, int64_t num_reqs, int64_t max_cols,
+                               int64_t row_stride, const int32_t* req_idx,
+                               const int64_t* positions, int64_t num_tokens, int32_t block_size,
+                               int64_t* slots, int32_t* err, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* key, int64_t key_stride, const void* value,
+                                    int64_t value_stride, int64_t num_tokens, int64_t row_bytes,
+                                    const int64_t* slots, void* cache, int64_t num_blocks,
+                                    int32_t block_size, int64_t block_stride,
+                                    int64_t token_stride, int64_t kv_stride, int32_t* err,
+                                    hipStream_t stream);
+
+hipError_t launch_build_xfer_list(const int32_t* src_ids, const int32_t* dst_ids,
+                                  const int64_t* req_offsets, int32_t num_reqs,
+                                  int64_t total_blocks, int32_t mode, kvx_xfer* xfers,
+                                  int64_t* xfer_count, int32_t* err, hipStream_t stream);
+
+// pack (to_buffer = true) or single-source unpack (to_buffer = false)
+hipError_t launch_copy_runs(bool to_buffer, void* const* layer_bases, int32_t num_layers,
+                            int64_t block_bytes, int64_t num_cache_blocks, const kvx_xfer* xfers,
+                            const int64_t* xfer_count, int64_t total_blocks, void* buffer,
+                            int32_t* err, hipStream_t stream);
+
+// unpack merging num_src >= 2 head-split sources
+hipError_t launch_merge_runs(const void* const* srcs, int32_t num_src, void* const* layer_bases,
+                             int32_t num_layers, int64_t block_bytes, int64_t num_cache_blocks,
+                             int32_t rows_per_block, const kvx_xfer* xfers,
+                             const int64_t* xfer_count, int64_t total_blocks, int32_t* err,
+                             hipStream_t stream);
+
+}  // namespace kvx

@@ -1,0 +1,91 @@
+"""Device-side setup shared by the GPU parity tests.
+
+Inputs come from `workloads`; expected values come only from `oracle` applied to host
+copies of those inputs (or to the oracle's own earlier outputs), never from the HIP path.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+import workloads as W
+
+DEV = "cuda:0"
+
+
+def log(msg: str):
+    print(f"[kvx-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def kvx():
+    from block_table_contiguous_amd import kvx as K
+    return K
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host_bytes(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+
+
+def layers_from_host(arrs, block_bytes):
+    """Per-layer uint8 [num_blocks][block_bytes] device tensors (separate allocations)."""
+    return [to_dev(np.ascontiguousarray(a).view(np.uint8).reshape(-1, block_bytes)) for a in arrs]
+
+
+class Transfer:
+    """A pack -> unpack round trip on the device for one TransferCase."""
+
+    def __init__(self, case: W.TransferCase, src_layers, dst_layers):
+        K = kvx()
+        self.K = K
+        self.case = case
+        self.src = src_layers
+        self.dst = dst_layers
+        self.L = len(src_layers)
+        self.BB = case.src_spec.block_bytes
+        self.nb_src = case.src_spec.num_blocks
+        self.nb_dst = case.dst_spec.num_blocks
+        self.N = case.total_blocks
+        self.src_bases = K.layer_base_table(src_layers)
+        self.dst_bases = K.layer_base_table(dst_layers)
+        self.src_ids, self.offsets = K.flatten_tables(case.src_tables, DEV)
+        self.dst_ids, _ = K.flatten_tables(case.dst_tables, DEV)
+        self.xp, self.cp = K.new_xfer_list(self.N, DEV)
+        self.xu, self.cu = K.new_xfer_list(self.N, DEV)
+        self.buf = torch.empty(max(self.L * self.N * self.BB, 16), dtype=torch.uint8, device=DEV)
+        self.err = torch.zeros(1, dtype=torch.int32, device=DEV)
+
+    def build(self):
+        K = self.K
+        K.kvx_build_xfer_list(self.src_ids, None, self.offsets, K.MODE_PACK, self.xp, self.cp, self.err)
+        K.kvx_build_xfer_list(None, self.dst_ids, self.offsets, K.MODE_UNPACK, self.xu, self.cu, self.err)
+
+    def pack(self):
+        self.K.kvx_pack(self.src_bases, self.BB, self.nb_src, self.xp, self.cp, self.N, self.buf, self.err)
+
+    def unpack(self):
+        self.K.kvx_unpack([self.buf], self.dst_bases, self.BB, self.nb_dst, 1, self.xu, self.cu, self.N,
+                          self.err)
+
+    def run(self):
+        self.build()
+        self.pack()
+        self.unpack()
+        torch.cuda.synchronize()
+
+    def err_bits(self) -> int:
+        return int(self.err.item())
+
+
+def check_runs_equal(K, xfers, count, expected):
+    got = K.decode_xfers(xfers, count)
+    assert len(got) == len(expected), (len(got), len(expected))
+    for i, (g, e) in enumerate(zip(got, expected)):
+        assert g == tuple(e), (i, g, e)

@@ -1,0 +1,129 @@
+"""The C ABI without a GPU: the library loads, exports every function include/kvx.h
+declares, and rejects bad arguments on the host before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvx.h")
+
+
+@pytest.fixture(scope="module")
+def kvx():
+    from block_table_contiguous_amd import kvx as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvx_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "kvx_abi_version", "kvx_build_xfer_list", "kvx_pack", "kvx_reshape_and_cache",
+        "kvx_slot_mapping", "kvx_status_string", "kvx_unpack"])
+
+
+def test_every_declared_symbol_is_exported(kvx):
+    for name in declared_functions():
+        assert hasattr(kvx.LIB, name), name
+        assert name in kvx.SIGNATURES, name
+
+
+def test_status_strings(kvx):
+    for code in range(5):
+        s = kvx.kvx_status_string(code)
+        assert s.startswith("kvx: ")
+    assert "unknown" in kvx.kvx_status_string(99)
+    assert kvx.kvx_abi_version() == 1
+
+
+def test_xfer_struct_size(kvx):
+    class Xfer(ctypes.Structure):
+        _fields_ = [("src_block", ctypes.c_int64), ("dst_block", ctypes.c_int64),
+                    ("buf_block", ctypes.c_int64), ("num_blocks", ctypes.c_int32), ("req", ctypes.c_int32)]
+    assert ctypes.sizeof(Xfer) == kvx.XFER_BYTES == 32
+
+
+P = 0x10000  # a fake, 16-byte aligned, non-null device address: never dereferenced here
+
+
+def call(kvx, name, *args):
+    return kvx._F[name](*args)
+
+
+def test_pack_validation(kvx):
+    ok = dict(bases=P, L=2, bb=8192, nb=100, x=P, cnt=P, n=10, buf=P)
+
+    def pack(**kw):
+        a = {**ok, **kw}
+        return call(kvx, "kvx_pack", a["bases"], a["L"], a["bb"], a["nb"], a["x"], a["cnt"], a["n"],
+                    a["buf"], None, None)
+    assert pack(L=-1) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert pack(bb=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert pack(n=-5) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert pack(n=1 << 31) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert pack(bases=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert pack(x=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert pack(bb=8200) == kvx.KVX_ERR_MISALIGNED
+    assert pack(buf=P + 8) == kvx.KVX_ERR_MISALIGNED
+    # empty work is a no-op that never reaches the device
+    assert pack(n=0, bases=None) == kvx.KVX_SUCCESS
+    assert pack(L=0) == kvx.KVX_SUCCESS
+
+
+def test_unpack_validation(kvx):
+    def unpack(S=1, srcs=(P,), bases=P, L=2, bb=8192, nb=100, rows=1, x=P, cnt=P, n=10):
+        arr = (ctypes.c_void_p * max(len(srcs), 1))(*srcs) if srcs is not None else None
+        return call(kvx, "kvx_unpack", arr, S, bases, L, bb, nb, rows, x, cnt, n, None, None)
+    assert unpack(S=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert unpack(S=9, srcs=(P,) * 9) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert unpack(rows=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert unpack(S=2, srcs=(P, P), rows=3, bb=64) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert unpack(S=2, srcs=(P, None), rows=32) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert unpack(S=2, srcs=(P, P + 16 * 3 + 8), rows=32) == kvx.KVX_ERR_MISALIGNED
+    assert unpack(bb=8200) == kvx.KVX_ERR_MISALIGNED
+    assert unpack(srcs=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert unpack(n=0) == kvx.KVX_SUCCESS
+
+
+def test_build_validation(kvx):
+    def build(src=P, dst=P, ro=P, R=2, n=10, mode=0, x=P, cap=10, cnt=P):
+        return call(kvx, "kvx_build_xfer_list", src, dst, ro, R, n, mode, x, cap, cnt, None, None)
+    assert build(mode=3) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert build(mode=-1) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert build(cap=9) == kvx.KVX_ERR_CAPACITY
+    assert build(R=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert build(src=None, mode=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert build(dst=None, mode=1) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert build(dst=None, mode=2) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert build(cnt=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert build(ro=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert build(x=P + 4) == kvx.KVX_ERR_MISALIGNED
+    assert build(n=-1) == kvx.KVX_ERR_INVALID_ARGUMENT
+
+
+def test_slot_and_reshape_validation(kvx):
+    def slots(bt=P, R=4, W=8, stride=8, rq=P, pos=P, T=10, bs=16, out=P):
+        return call(kvx, "kvx_slot_mapping", bt, R, W, stride, rq, pos, T, bs, out, None, None)
+    assert slots(bs=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert slots(T=-1) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert slots(W=9) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert slots(out=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert slots(T=0, out=None) == kvx.KVX_SUCCESS
+
+    def rc(k=P, ks=4096, v=P, vs=4096, T=10, row=2048, sm=P, c=P, nb=64, bs=16,
+           bst=65536, tst=4096, kst=2048):
+        return call(kvx, "kvx_reshape_and_cache", k, ks, v, vs, T, row, sm, c, nb, bs, bst, tst, kst,
+                    None, None)
+    assert rc(row=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert rc(bs=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert rc(sm=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert rc(k=P + 2) == kvx.KVX_ERR_MISALIGNED
+    assert rc(row=2040) == kvx.KVX_ERR_MISALIGNED
+    assert rc(kst=2056) == kvx.KVX_ERR_MISALIGNED
+    assert rc(T=0) == kvx.KVX_SUCCESS

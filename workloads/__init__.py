@@ -312,16 +312,19 @@ def asym_tp(seed: int = ASYM_SEED, num_layers: int = 32, num_reqs: int = 16,
 
 def random_transfer(seed: int, num_layers: int, num_blocks: int, block_size: int,
                     num_kv_heads: int, head_dim: int, lengths, elem_bytes: int = 2,
-                    run_p: float = 0.5, slot: int = 8, with_caches: bool = True) -> TransferCase:
+                    run_p: float = 0.5, slot: Optional[int] = None,
+                    with_caches: bool = True) -> TransferCase:
     """A host-sized random round trip: requests of the given token lengths (0 allowed), source
-    tables with geometric(run_p) runs in random `slot`-block slots (needs about
-    num_blocks/slot >= number of runs), destination ids from a permutation.
+    tables with geometric(run_p) runs in random `slot`-block slots (by default the largest
+    slot <= 8 that leaves one slot per block), destination ids from a permutation.
     Source caches random words; destination caches the sentinel."""
     spec = PagedSpec(num_layers, num_blocks, block_size, num_kv_heads, head_dim, elem_bytes)
     rng = np.random.default_rng(seed)
     counts = [blocks_for(n, block_size) for n in lengths]
     if sum(counts) > num_blocks:
         raise ValueError("requests do not fit the cache")
+    if slot is None:
+        slot = max(1, min(8, num_blocks // max(sum(counts), 1)))
     src_tables = fragmented_tables(rng, num_blocks, len(counts), counts, slot=slot, p=run_p)
     dst_tables = pop_tables(rng.permutation(num_blocks), counts)
     src_caches = dst_caches = None
