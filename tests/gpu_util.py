@@ -31,7 +31,8 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
 
 
 def host_bytes(t: torch.Tensor) -> np.ndarray:
-    return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+    """Flat uint8 host copy of a device tensor's bytes."""
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy().reshape(-1)
 
 
 def layers_from_host(arrs, block_bytes):

@@ -76,8 +76,8 @@ def test_many_blocks_several_scan_tiles():
     """> 4 tiles of the run-list scan (4096 positions per tile), many requests, empty ones,
     small blocks so every wavefront spans many runs."""
     rng = np.random.default_rng(77)
-    lengths = [int(x) for x in rng.integers(0, 120, size=900)]
-    for i in range(0, 900, 37):
+    lengths = [int(x) for x in rng.integers(0, 160, size=1000)]
+    for i in range(0, 1000, 37):
         lengths[i] = 0
     case = W.random_transfer(78, 2, 60000, 4, 1, 8, lengths, run_p=0.3)
     assert case.total_blocks > 4 * 4096
