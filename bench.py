@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ops", action="store_true")
     ap.add_argument("--op-reps", type=int, default=10)
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured HIP graph (reported as graph_ms_per_step)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -205,6 +207,27 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step")
 
+    graph_ms = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        log(f"graph replay: {graph_ms:.4f} ms/step")
+        assert int(err.item()) == 0, "device error flag raised"
+
     copy_bytes = 2 * L * N * BB                    # pack and unpack: each byte read once, written once
     write_bytes = L * R * (2 * 2 * row + 8)        # new-token write: K,V read+write + slot
     slot_bytes = R * (4 + 8 + 4 + 8)               # req index, position, table entry, slot
@@ -269,6 +292,7 @@ def main():
             "parallelism": "single GPU",
         },
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "ops": out_ops,

@@ -32,9 +32,11 @@ static int64_t env_i64(const char* name, int64_t dflt) {
 
 const Tuning& tuning() {
   static const Tuning t = {
-      env_i64("KVX_WAVE_BYTES", 64 * 1024),
+      {env_i64("KVX_WAVE_BYTES_PACK", 8 * 1024), (int)env_i64("KVX_NT_PACK", 3)},
+      {env_i64("KVX_WAVE_BYTES_UNPACK", 8 * 1024), (int)env_i64("KVX_NT_UNPACK", 3)},
+      {env_i64("KVX_WAVE_BYTES_MERGE", 64 * 1024), (int)env_i64("KVX_NT_MERGE", 3)},
       (int)env_i64("KVX_XCD_REMAP", 1),
-      (int)env_i64("KVX_NT", 0),
+      (int)env_i64("KVX_ONE_BATCH", 1),
   };
   return t;
 }
@@ -45,6 +47,28 @@ const Tuning& tuning() {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define KVX_GLOBAL __attribute__((address_space(1)))
+// Read-only view of memory no kernel writes while it runs (run list, layer bases, counts):
+// uniform loads through it become scalar loads, which wait on lgkmcnt and so never stall
+// behind the vector loads of the data being copied.
+#define KVX_CONST __attribute__((address_space(4)))
+
+template <class T>
+__device__ __forceinline__ const KVX_CONST T* readonly(const T* p) {
+  return (const KVX_CONST T*)p;
+}
+
+// One run, read field by field through the read-only view.
+struct Run {
+  int64_t src, dst, buf, n;
+};
+__device__ __forceinline__ Run load_run(const KVX_CONST kvx_xfer* xf, int64_t k) {
+  Run r;
+  r.src = xf[k].src_block;
+  r.dst = xf[k].dst_block;
+  r.buf = xf[k].buf_block;
+  r.n = xf[k].num_blocks;
+  return r;
+}
 
 constexpr int kWave = 64;
 constexpr int kVec = 16;                 // bytes per lane access
@@ -183,8 +207,21 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const int64_t wave = uniform((int64_t)blockIdx.x * waves_per_wg + (threadIdx.x / kWave));
   const int64_t num_waves = (int64_t)gridDim.x * waves_per_wg;
   const int64_t nvec = row_bytes / kVec;  // vectors in one row
+  const int64_t nv2 = 2 * nvec;           // vector q < nvec is in the K row, else in the V row
+  const KVX_CONST int64_t* sl = readonly(slots);
   for (int64_t t = wave; t < num_tokens; t += num_waves) {
-    const int64_t s = uniform(slots[t]);
+    const char* krow = key + t * key_stride;
+    const char* vrow = value + t * value_stride;
+    // The rows do not depend on the slot: their first batch is in flight before the slot
+    // arrives. Lanes past the rows re-read vector 0 so every load is unconditional.
+    u32x4 v[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      int64_t q = (int64_t)j * kWave + lane;
+      q = q < nv2 ? q : 0;
+      v[j] = load16<false>(q < nvec ? krow + q * kVec : vrow + (q - nvec) * kVec);
+    }
+    const int64_t s = sl[t];
     if (s < 0) continue;  // padding token
     int64_t blk, off;
     if (s <= 0x7fffffff) {
@@ -198,22 +235,25 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
       if (lane == 0) raise_error(err, KVX_DEVERR_SLOT_RANGE);
       continue;
     }
-    char* base = cache + blk * block_stride + off * token_stride;
-    const char* krow = key + t * key_stride;
-    const char* vrow = value + t * value_stride;
-    // vectors q in [0, 2*nvec): q < nvec -> K row, else V row
-    for (int64_t q0 = 0; q0 < 2 * nvec; q0 += (int64_t)K * kWave) {
-      u32x4 v[K];
+    char* kdst = cache + blk * block_stride + off * token_stride;
+    char* vdst = kdst + kv_stride;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t q = (int64_t)j * kWave + lane;
+      if (q < nv2) store16<false>(q < nvec ? kdst + q * kVec : vdst + (q - nvec) * kVec, v[j]);
+    }
+    // rows longer than one batch (over K*64 vectors for K and V together)
+    for (int64_t q0 = (int64_t)K * kWave; q0 < nv2; q0 += (int64_t)K * kWave) {
 #pragma unroll
       for (int j = 0; j < K; ++j) {
-        const int64_t q = q0 + j * kWave + lane;
-        if (q < 2 * nvec) v[j] = load16<false>(q < nvec ? krow + q * kVec : vrow + (q - nvec) * kVec);
+        int64_t q = q0 + j * kWave + lane;
+        q = q < nv2 ? q : 0;
+        v[j] = load16<false>(q < nvec ? krow + q * kVec : vrow + (q - nvec) * kVec);
       }
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         const int64_t q = q0 + j * kWave + lane;
-        if (q < 2 * nvec)
-          store16<false>(q < nvec ? base + q * kVec : base + kv_stride + (q - nvec) * kVec, v[j]);
+        if (q < nv2) store16<false>(q < nvec ? kdst + q * kVec : vdst + (q - nvec) * kVec, v[j]);
       }
     }
   }
@@ -223,13 +263,15 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 // a3 — transfer list: run-start flags -> workgroup prefix scan -> compaction
 // --------------------------------------------------------------------------------------
 
-constexpr int kScanThreads = 1024;
-constexpr int kScanItems = 4;
+constexpr int kScanThreads = 512;
+constexpr int kScanItems = 16;
 constexpr int kScanTile = kScanThreads * kScanItems;
 constexpr int kScanWaves = kScanThreads / kWave;
+constexpr int kLdsOffsets = 4096;  // request offsets staged in LDS when num_reqs < this
 
-// Largest r in [0, R) with req_offsets[r] <= p (0 if none).
-__device__ __forceinline__ int32_t find_request(const int64_t* __restrict__ ro, int32_t R, int64_t p) {
+// Largest r in [0, R) with ro[r] <= p (0 if none).
+template <class P>
+__device__ __forceinline__ int32_t find_request(P ro, int32_t R, int64_t p) {
   int32_t lo = 0, hi = R - 1;
   while (lo < hi) {
     const int32_t mid = (lo + hi + 1) >> 1;
@@ -239,104 +281,130 @@ __device__ __forceinline__ int32_t find_request(const int64_t* __restrict__ ro, 
   return lo;
 }
 
-// Single workgroup of 1024 threads walks the blocks in tiles of 4096. Per tile: every thread
-// flags run starts among its 4 consecutive positions, a wave scan (DPP shuffles) plus a
-// 16-entry LDS pass turns the flags into run indices, and each thread writes the runs it
-// starts and the lengths of the runs it ends. The scan carries two quantities: the number of
-// starts so far (the run index) and the position of the latest start (for run lengths).
+// One tile of positions [tile, tile + kScanTile): every thread flags run starts among its
+// kScanItems consecutive positions (loading one id before and one after them), a wave scan
+// (shuffles) plus a 16-entry LDS pass turns the flags into run indices, and each thread
+// writes the runs it starts and the lengths of the runs it ends. The scan carries two
+// quantities: the number of starts so far (the run index) and the position of the latest
+// start (for run lengths), so no thread ever reads another thread's output.
+template <class P>
+__device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
+                                           const int32_t* __restrict__ dst, P ro, int32_t R,
+                                           int64_t N, bool use_src, bool use_dst, int64_t tile,
+                                           kvx_xfer* __restrict__ out, int64_t* s_cnt,
+                                           int64_t* s_last, int64_t& carry_cnt,
+                                           int64_t& carry_last) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  const int64_t p0 = tile + (int64_t)tid * kScanItems;
+  int32_t sv[kScanItems + 2], dv[kScanItems + 2];  // ids at p0-1 .. p0+kScanItems
+#pragma unroll
+  for (int i = 0; i < kScanItems + 2; ++i) {
+    const int64_t p = p0 - 1 + i;
+    const bool in = p >= 0 && p < N;
+    sv[i] = (use_src && in) ? src[p] : 0;
+    dv[i] = (use_dst && in) ? dst[p] : 0;
+  }
+  int32_t r = (p0 < N) ? find_request(ro, R, p0) : 0;
+  bool st[kScanItems + 1];
+  int32_t rq[kScanItems];
+  int64_t cnt = 0, last = -1;
+#pragma unroll
+  for (int i = 0; i <= kScanItems; ++i) {
+    const int64_t p = p0 + i;
+    bool f = false;
+    if (p < N) {
+      while (r + 1 < R && ro[r + 1] <= p) ++r;
+      f = (p == 0) || (p == ro[r]) ||
+          (use_src && (int64_t)sv[i + 1] != (int64_t)sv[i] + 1) ||
+          (use_dst && (int64_t)dv[i + 1] != (int64_t)dv[i] + 1);
+    }
+    st[i] = f;
+    if (i < kScanItems) {
+      rq[i] = r;
+      if (f) { ++cnt; last = p; }
+    }
+  }
+
+  // workgroup scan of (cnt: sum, last: max)
+  int64_t ci = cnt, li = last;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int64_t c = __shfl_up(ci, d, kWave);
+    const int64_t l = __shfl_up(li, d, kWave);
+    if (lane >= d) { ci += c; li = l > li ? l : li; }
+  }
+  int64_t li_excl = __shfl_up(li, 1, kWave);
+  if (lane == 0) li_excl = -1;
+  if (lane == kWave - 1) { s_cnt[wid] = ci; s_last[wid] = li; }
+  __syncthreads();
+  int64_t c_before = 0, l_before = -1, c_tile = 0, l_tile = -1;
+#pragma unroll
+  for (int w = 0; w < kScanWaves; ++w) {
+    const int64_t c = s_cnt[w], l = s_last[w];
+    if (w < wid) { c_before += c; l_before = l > l_before ? l : l_before; }
+    c_tile += c;
+    l_tile = l > l_tile ? l : l_tile;
+  }
+  __syncthreads();
+
+  int64_t k = carry_cnt + c_before + (ci - cnt);
+  int64_t cur = carry_last;
+  if (l_before > cur) cur = l_before;
+  if (li_excl > cur) cur = li_excl;
+#pragma unroll
+  for (int i = 0; i < kScanItems; ++i) {
+    const int64_t p = p0 + i;
+    if (p < N) {
+      if (st[i]) {
+        kvx_xfer* x = out + k;
+        x->src_block = use_src ? sv[i + 1] : p;
+        x->dst_block = use_dst ? dv[i + 1] : p;
+        x->buf_block = p;
+        x->req = rq[i];
+        cur = p;
+        ++k;
+      }
+      if (p == N - 1 || st[i + 1]) out[k - 1].num_blocks = (int32_t)(p - cur + 1);
+    }
+  }
+  carry_cnt += c_tile;
+  if (l_tile > carry_last) carry_last = l_tile;
+}
+
+// A single workgroup of 512 threads walks the blocks tile by tile (8192 positions per tile).
+// When there are fewer than 4096 requests their offsets are staged in LDS first, so the
+// per-position request lookups never wait on global memory.
 __global__ __launch_bounds__(kScanThreads) void build_xfer_kernel(
     const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
     const int64_t* __restrict__ ro, int32_t R, int64_t N, int32_t mode,
     kvx_xfer* __restrict__ out, int64_t* __restrict__ count, int32_t* err) {
   __shared__ int64_t s_cnt[kScanWaves];
   __shared__ int64_t s_last[kScanWaves];
+  __shared__ int64_t s_ro[kLdsOffsets + 1];
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wid = tid / kWave;
   const bool use_src = mode != KVX_MODE_UNPACK;
   const bool use_dst = mode != KVX_MODE_PACK;
+  const bool in_lds = R < kLdsOffsets;
 
   // CSR sanity: ro[0] == 0, non-decreasing, ro[R] == N
-  for (int32_t i = tid; i < R; i += kScanThreads)
-    if (ro[i + 1] < ro[i]) raise_error(err, KVX_DEVERR_OFFSETS);
+  for (int32_t i = tid; i <= R; i += kScanThreads) {
+    const int64_t v = ro[i];
+    if (in_lds) s_ro[i] = v;
+    if (i < R && ro[i + 1] < v) raise_error(err, KVX_DEVERR_OFFSETS);
+  }
   if (tid == 0 && (ro[0] != 0 || ro[R] != N)) raise_error(err, KVX_DEVERR_OFFSETS);
+  __syncthreads();
 
   int64_t carry_cnt = 0, carry_last = -1;
   for (int64_t tile = 0; tile < N; tile += kScanTile) {
-    const int64_t p0 = tile + (int64_t)tid * kScanItems;
-    // ids at p0-1 .. p0+kScanItems (one before for the step test, one after for run ends)
-    int64_t sv[kScanItems + 2], dv[kScanItems + 2];
-#pragma unroll
-    for (int i = 0; i < kScanItems + 2; ++i) {
-      const int64_t p = p0 - 1 + i;
-      const bool in = p >= 0 && p < N;
-      sv[i] = (use_src && in) ? (int64_t)src[p] : 0;
-      dv[i] = (use_dst && in) ? (int64_t)dst[p] : 0;
-    }
-    int32_t r = (p0 < N) ? find_request(ro, R, p0) : 0;
-    bool st[kScanItems + 1];
-    int32_t rq[kScanItems];
-    int64_t cnt = 0, last = -1;
-#pragma unroll
-    for (int i = 0; i <= kScanItems; ++i) {
-      const int64_t p = p0 + i;
-      bool s = false;
-      if (p < N) {
-        while (r + 1 < R && ro[r + 1] <= p) ++r;
-        s = (p == 0) || (p == ro[r]) || (use_src && sv[i + 1] != sv[i] + 1) ||
-            (use_dst && dv[i + 1] != dv[i] + 1);
-      }
-      st[i] = s;
-      if (i < kScanItems) {
-        rq[i] = r;
-        if (s) { ++cnt; last = p; }
-      }
-    }
-
-    // workgroup scan of (cnt: sum, last: max)
-    int64_t ci = cnt, li = last;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int64_t c = __shfl_up(ci, d, kWave);
-      const int64_t l = __shfl_up(li, d, kWave);
-      if (lane >= d) { ci += c; li = l > li ? l : li; }
-    }
-    int64_t li_excl = __shfl_up(li, 1, kWave);
-    if (lane == 0) li_excl = -1;
-    if (lane == kWave - 1) { s_cnt[wid] = ci; s_last[wid] = li; }
-    __syncthreads();
-    int64_t c_before = 0, l_before = -1, c_tile = 0, l_tile = -1;
-#pragma unroll
-    for (int w = 0; w < kScanWaves; ++w) {
-      const int64_t c = s_cnt[w], l = s_last[w];
-      if (w < wid) { c_before += c; l_before = l > l_before ? l : l_before; }
-      c_tile += c;
-      l_tile = l > l_tile ? l : l_tile;
-    }
-    __syncthreads();
-
-    int64_t k = carry_cnt + c_before + (ci - cnt);
-    int64_t cur = carry_last;
-    if (l_before > cur) cur = l_before;
-    if (li_excl > cur) cur = li_excl;
-#pragma unroll
-    for (int i = 0; i < kScanItems; ++i) {
-      const int64_t p = p0 + i;
-      if (p < N) {
-        if (st[i]) {
-          kvx_xfer* x = out + k;
-          x->src_block = use_src ? sv[i + 1] : p;
-          x->dst_block = use_dst ? dv[i + 1] : p;
-          x->buf_block = p;
-          x->req = rq[i];
-          cur = p;
-          ++k;
-        }
-        if (p == N - 1 || st[i + 1]) out[k - 1].num_blocks = (int32_t)(p - cur + 1);
-      }
-    }
-    carry_cnt += c_tile;
-    if (l_tile > carry_last) carry_last = l_tile;
+    if (in_lds)
+      build_tile<const int64_t*>(src, dst, s_ro, R, N, use_src, use_dst, tile, out, s_cnt, s_last,
+                                 carry_cnt, carry_last);
+    else
+      build_tile<const int64_t*>(src, dst, ro, R, N, use_src, use_dst, tile, out, s_cnt, s_last,
+                                 carry_cnt, carry_last);
   }
   if (tid == 0) *count = carry_cnt;
 }
@@ -364,7 +432,11 @@ struct RunCopyArgs {
 
 constexpr int kCopyThreads = 256;
 constexpr int kCopyWavesPerWg = kCopyThreads / kWave;
-constexpr int kCopyBatch = 8;  // 1 KiB loads in flight per lane batch = 8 KiB per wavefront
+#ifndef KVX_COPY_BATCH
+#define KVX_COPY_BATCH 8
+#endif
+// 1 KiB wavefront loads a lane issues before its stores (8 -> 8 KiB in flight per wavefront)
+constexpr int kCopyBatch = KVX_COPY_BATCH;
 
 // Work split: wavefront w owns layer l = w / waves_per_layer and buffer positions
 // [c*B, min((c+1)*B, N)) of that layer (B = blocks_per_wave), so every wavefront moves the
@@ -519,6 +591,163 @@ __global__ __launch_bounds__(kCopyThreads) void merge_runs_kernel(MergeArgs a) {
 }
 
 // --------------------------------------------------------------------------------------
+// one-batch fast paths (block rows in whole KiB)
+// --------------------------------------------------------------------------------------
+
+// Bytes one wavefront moves in the fast paths: one batch of kCopyBatch 1 KiB instructions.
+constexpr int64_t kUnitBytes = (int64_t)kCopyBatch * kWaveBytes;
+
+// Pack / single-source unpack when block_bytes is a multiple of 1 KiB (a 16-token block of
+// K,V x heads x head_dim x 2 B always is). Wavefront w owns kUnitBytes of one layer's buffer
+// slice; each of its kCopyBatch instruction slots lies inside one block. The slot addresses
+// are worked out on the scalar unit (walking the runs from the one holding the first block),
+// then the wavefront issues all its loads, then all its stores, and exits. On this
+// architecture stores count in vmcnt, so a wavefront with a second batch would wait for its
+// first batch's store acknowledgements; one batch per wavefront never does.
+template <bool TO_BUFFER, bool NTL, bool NTS>
+__global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(RunCopyArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t wg = blockIdx.x;
+  if (a.xcd_remap) wg = xcd_slice_order(wg, a.num_wgs);
+  const int64_t w = uniform(wg * kCopyWavesPerWg + (threadIdx.x / kWave));
+  if (w >= a.total_waves) return;
+  const int64_t l = w / a.waves_per_layer;
+  const int64_t u = w - l * a.waves_per_layer;
+  const int64_t N = a.total_blocks;
+  const int64_t BB = a.block_bytes;
+  const int64_t layer_bytes = N * BB;
+  const KVX_CONST kvx_xfer* xf = readonly(a.xfers);
+  int64_t count = *readonly(a.xfer_count);
+  if (count > N) count = N;
+  if (count <= 0) return;
+  char* cache = const_cast<char*>(*readonly(a.layer_bases + l));
+  char* buf = a.buffer + l * layer_bytes;
+
+  const int64_t o0 = u * kUnitBytes;
+  int64_t q = o0 / BB;       // buffer position of the first slot
+  int64_t off = o0 - q * BB; // byte offset inside that block (a multiple of 1 KiB)
+  int64_t k = uniform(find_run(a.xfers, count, q, lane));
+  if (k < 0) k = 0;
+  Run x = load_run(xf, k);
+  // Slots with nothing to move load from `idle` (1 KiB of this wavefront's own buffer range,
+  // always inside the allocation) so every load is unconditional; only stores are skipped.
+  const char* idle = buf + o0;
+  const char* sp[kCopyBatch];
+  char* dp[kCopyBatch];
+  bool on[kCopyBatch];
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < kCopyBatch; ++j) {
+    const int64_t o = o0 + (int64_t)j * kWaveBytes;
+    on[j] = false;
+    sp[j] = idle;
+    dp[j] = nullptr;
+    if (o < layer_bytes) {
+      while (x.buf + x.n <= q && k + 1 < count) x = load_run(xf, ++k);
+      if (q >= x.buf && q < x.buf + x.n) {
+        const int64_t id = (TO_BUFFER ? x.src : x.dst) + (q - x.buf);
+        if (id >= 0 && id < a.num_cache_blocks) {
+          char* c = cache + id * BB + off;
+          char* b = buf + o;
+          sp[j] = TO_BUFFER ? c : b;
+          dp[j] = TO_BUFFER ? b : c;
+          on[j] = true;
+        } else {
+          bad = true;
+        }
+      }
+    }
+    off += kWaveBytes;
+    if (off == BB) { off = 0; ++q; }
+  }
+  u32x4 v[kCopyBatch];
+#pragma unroll
+  for (int j = 0; j < kCopyBatch; ++j) v[j] = load16<NTL>(sp[j] + lane * kVec);
+#pragma unroll
+  for (int j = 0; j < kCopyBatch; ++j)
+    if (on[j]) store16<NTS>(dp[j] + lane * kVec, v[j]);
+  if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_BLOCK_RANGE);
+}
+
+// Head merge when a source row is a multiple of 1 KiB. Wavefront w owns kUnitBytes of one
+// layer's destination bytes taken in buffer order (position q, then row, then source, then
+// byte); slot j is the 1 KiB piece at destination offset w_in of block q, which is bytes
+// [xo, xo + 1 KiB) of row `row` of source s. Counters step (xo, s, row, q) without divisions.
+template <bool NTL, bool NTS>
+__global__ __launch_bounds__(kCopyThreads) void merge_slots_kernel(MergeArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t wg = blockIdx.x;
+  if (a.xcd_remap) wg = xcd_slice_order(wg, a.num_wgs);
+  const int64_t w = uniform(wg * kCopyWavesPerWg + (threadIdx.x / kWave));
+  if (w >= a.total_waves) return;
+  const int64_t l = w / a.waves_per_layer;
+  const int64_t u = w - l * a.waves_per_layer;
+  const int64_t N = a.total_blocks;
+  const int64_t S = a.num_src;
+  const int64_t BB = a.block_bytes;
+  const int64_t BBs = BB / S;
+  const int64_t row_src = a.row_src;
+  const int64_t row_dst = row_src * S;
+  const int64_t layer_bytes = N * BB;
+  const KVX_CONST kvx_xfer* xf = readonly(a.xfers);
+  int64_t count = *readonly(a.xfer_count);
+  if (count > N) count = N;
+  if (count <= 0) return;
+  char* cache = const_cast<char*>(*readonly(a.layer_bases + l));
+
+  const int64_t o0 = u * kUnitBytes;
+  int64_t q = o0 / BB;
+  int64_t w_in = o0 - q * BB;
+  int64_t row = w_in / row_dst;
+  int64_t rem = w_in - row * row_dst;
+  int64_t s = rem / row_src;
+  int64_t xo = rem - s * row_src;
+  int64_t k = uniform(find_run(a.xfers, count, q, lane));
+  if (k < 0) k = 0;
+  Run x = load_run(xf, k);
+  // Idle slots load from the first KiB of source 0's layer slice (always in bounds).
+  const char* idle = a.src[0] + l * N * BBs;
+  const char* sp[kCopyBatch];
+  char* dp[kCopyBatch];
+  bool on[kCopyBatch];
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < kCopyBatch; ++j) {
+    const int64_t o = o0 + (int64_t)j * kWaveBytes;
+    on[j] = false;
+    sp[j] = idle;
+    dp[j] = nullptr;
+    if (o < layer_bytes) {
+      while (x.buf + x.n <= q && k + 1 < count) x = load_run(xf, ++k);
+      if (q >= x.buf && q < x.buf + x.n) {
+        const int64_t id = x.dst + (q - x.buf);
+        if (id >= 0 && id < a.num_cache_blocks) {
+          sp[j] = a.src[s] + (l * N + q) * BBs + row * row_src + xo;
+          dp[j] = cache + id * BB + w_in;
+          on[j] = true;
+        } else {
+          bad = true;
+        }
+      }
+    }
+    xo += kWaveBytes;
+    w_in += kWaveBytes;
+    if (xo == row_src) {
+      xo = 0;
+      if (++s == S) { s = 0; ++row; }
+    }
+    if (w_in == BB) { w_in = 0; row = 0; s = 0; xo = 0; ++q; }
+  }
+  u32x4 v[kCopyBatch];
+#pragma unroll
+  for (int j = 0; j < kCopyBatch; ++j) v[j] = load16<NTL>(sp[j] + lane * kVec);
+#pragma unroll
+  for (int j = 0; j < kCopyBatch; ++j)
+    if (on[j]) store16<NTS>(dp[j] + lane * kVec, v[j]);
+  if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_BLOCK_RANGE);
+}
+
+// --------------------------------------------------------------------------------------
 // launchers
 // --------------------------------------------------------------------------------------
 
@@ -561,22 +790,37 @@ hipError_t launch_build_xfer_list(const int32_t* src_ids, const int32_t* dst_ids
 
 // Blocks per wavefront: about wave_bytes of buffer each, and few enough wavefronts that the
 // grid stays well inside 32-bit workgroup counts.
-static int64_t blocks_per_wave_for(int64_t block_bytes, int64_t num_layers, int64_t N) {
-  int64_t bpw = tuning().wave_bytes / block_bytes;
+static int64_t blocks_per_wave_for(int64_t wave_bytes, int64_t block_bytes, int64_t num_layers,
+                                   int64_t N) {
+  int64_t bpw = wave_bytes / block_bytes;
   if (bpw < 1) bpw = 1;
   const int64_t max_waves = (int64_t)1 << 30;
   const int64_t min_bpw = ceil_div(num_layers * N, max_waves);
   return bpw > min_bpw ? bpw : min_bpw;
 }
 
+template <bool TO_BUFFER, bool NTL, bool NTS>
+static void launch_copy_policy(const RunCopyArgs& a, bool slots, unsigned grid, hipStream_t stream) {
+  if (slots) copy_slots_kernel<TO_BUFFER, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
+  else copy_runs_kernel<TO_BUFFER, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
+}
+
 template <bool TO_BUFFER>
-static void launch_copy_variant(const RunCopyArgs& a, unsigned grid, hipStream_t stream) {
-  switch (tuning().nt_mode & 3) {
-    case 0: copy_runs_kernel<TO_BUFFER, false, false><<<grid, kCopyThreads, 0, stream>>>(a); break;
-    case 1: copy_runs_kernel<TO_BUFFER, true, false><<<grid, kCopyThreads, 0, stream>>>(a); break;
-    case 2: copy_runs_kernel<TO_BUFFER, false, true><<<grid, kCopyThreads, 0, stream>>>(a); break;
-    default: copy_runs_kernel<TO_BUFFER, true, true><<<grid, kCopyThreads, 0, stream>>>(a); break;
+static void launch_copy_variant(const RunCopyArgs& a, int nt_mode, bool slots, unsigned grid,
+                                hipStream_t stream) {
+  switch (nt_mode & 3) {
+    case 0: launch_copy_policy<TO_BUFFER, false, false>(a, slots, grid, stream); break;
+    case 1: launch_copy_policy<TO_BUFFER, true, false>(a, slots, grid, stream); break;
+    case 2: launch_copy_policy<TO_BUFFER, false, true>(a, slots, grid, stream); break;
+    default: launch_copy_policy<TO_BUFFER, true, true>(a, slots, grid, stream); break;
   }
+}
+
+// The one-batch fast path needs whole-KiB blocks and a grid that fits 32-bit workgroup ids.
+static bool use_slots(int64_t unit_bytes_ok, int64_t num_layers, int64_t layer_bytes) {
+  if (!unit_bytes_ok || !tuning().one_batch) return false;
+  const int64_t waves = num_layers * ceil_div(layer_bytes, kUnitBytes);
+  return ceil_div(waves, kCopyWavesPerWg) < ((int64_t)1 << 31);
 }
 
 hipError_t launch_copy_runs(bool to_buffer, void* const* layer_bases, int32_t num_layers,
@@ -592,15 +836,22 @@ hipError_t launch_copy_runs(bool to_buffer, void* const* layer_bases, int32_t nu
   a.block_bytes = block_bytes;
   a.num_cache_blocks = num_cache_blocks;
   a.total_blocks = total_blocks;
-  a.blocks_per_wave = blocks_per_wave_for(block_bytes, num_layers, total_blocks);
-  a.waves_per_layer = ceil_div(total_blocks, a.blocks_per_wave);
+  const CopyTuning& ct = to_buffer ? tuning().pack : tuning().unpack;
+  const bool slots = use_slots(block_bytes % kWaveBytes == 0, num_layers, total_blocks * block_bytes);
+  if (slots) {  // one kUnitBytes batch per wavefront
+    a.blocks_per_wave = 0;
+    a.waves_per_layer = ceil_div(total_blocks * block_bytes, kUnitBytes);
+  } else {      // general path: whole blocks, about wave_bytes per wavefront
+    a.blocks_per_wave = blocks_per_wave_for(ct.wave_bytes, block_bytes, num_layers, total_blocks);
+    a.waves_per_layer = ceil_div(total_blocks, a.blocks_per_wave);
+  }
   a.total_waves = a.waves_per_layer * num_layers;
   a.num_wgs = ceil_div(a.total_waves, kCopyWavesPerWg);
   a.num_layers = num_layers;
   a.xcd_remap = tuning().xcd_remap;
   const unsigned grid = (unsigned)a.num_wgs;
-  if (to_buffer) launch_copy_variant<true>(a, grid, stream);
-  else launch_copy_variant<false>(a, grid, stream);
+  if (to_buffer) launch_copy_variant<true>(a, ct.nt_mode, slots, grid, stream);
+  else launch_copy_variant<false>(a, ct.nt_mode, slots, grid, stream);
   return hipGetLastError();
 }
 
@@ -619,8 +870,15 @@ hipError_t launch_merge_runs(const void* const* srcs, int32_t num_src, void* con
   a.num_cache_blocks = num_cache_blocks;
   a.total_blocks = total_blocks;
   a.row_src = block_bytes / ((int64_t)rows_per_block * num_src);
-  a.blocks_per_wave = blocks_per_wave_for(block_bytes, num_layers, total_blocks);
-  a.waves_per_layer = ceil_div(total_blocks, a.blocks_per_wave);
+  const bool slots = use_slots(a.row_src % kWaveBytes == 0, num_layers, total_blocks * block_bytes);
+  if (slots) {
+    a.blocks_per_wave = 0;
+    a.waves_per_layer = ceil_div(total_blocks * block_bytes, kUnitBytes);
+  } else {
+    a.blocks_per_wave = blocks_per_wave_for(tuning().merge.wave_bytes, block_bytes, num_layers,
+                                            total_blocks);
+    a.waves_per_layer = ceil_div(total_blocks, a.blocks_per_wave);
+  }
   a.total_waves = a.waves_per_layer * num_layers;
   a.num_wgs = ceil_div(a.total_waves, kCopyWavesPerWg);
   a.num_src = num_src;
@@ -628,12 +886,16 @@ hipError_t launch_merge_runs(const void* const* srcs, int32_t num_src, void* con
   a.num_layers = num_layers;
   a.xcd_remap = tuning().xcd_remap;
   const unsigned grid = (unsigned)a.num_wgs;
-  switch (tuning().nt_mode & 3) {
-    case 0: merge_runs_kernel<false, false><<<grid, kCopyThreads, 0, stream>>>(a); break;
-    case 1: merge_runs_kernel<true, false><<<grid, kCopyThreads, 0, stream>>>(a); break;
-    case 2: merge_runs_kernel<false, true><<<grid, kCopyThreads, 0, stream>>>(a); break;
-    default: merge_runs_kernel<true, true><<<grid, kCopyThreads, 0, stream>>>(a); break;
+#define KVX_MERGE_LAUNCH(NTL, NTS)                                                  \
+  if (slots) merge_slots_kernel<NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);   \
+  else merge_runs_kernel<NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
+  switch (tuning().merge.nt_mode & 3) {
+    case 0: KVX_MERGE_LAUNCH(false, false) break;
+    case 1: KVX_MERGE_LAUNCH(true, false) break;
+    case 2: KVX_MERGE_LAUNCH(false, true) break;
+    default: KVX_MERGE_LAUNCH(true, true) break;
   }
+#undef KVX_MERGE_LAUNCH
   return hipGetLastError();
 }
 

@@ -11,10 +11,16 @@ namespace kvx {
 
 // Launch-shape knobs. Defaults are compiled in; each can be overridden once per process
 // through the environment (read on first use) so sweeps need no rebuild.
+// Per copy kernel: bytes of buffer one wavefront owns, and the cache policy
+// (bit 0: non-temporal loads, bit 1: non-temporal stores).
+struct CopyTuning {
+  int64_t wave_bytes;  // KVX_WAVE_BYTES_{PACK,UNPACK,MERGE}
+  int nt_mode;         // KVX_NT_{PACK,UNPACK,MERGE}
+};
 struct Tuning {
-  int64_t wave_bytes;  // bytes of buffer one wavefront owns in pack/unpack (KVX_WAVE_BYTES)
-  int xcd_remap;       // 1: give each XCD a contiguous slice of the work (KVX_XCD_REMAP)
-  int nt_mode;         // bit 0: non-temporal loads, bit 1: non-temporal stores (KVX_NT)
+  CopyTuning pack, unpack, merge;
+  int xcd_remap;  // 1: give each XCD a contiguous slice of the work (KVX_XCD_REMAP)
+  int one_batch;  // 1: one-batch-per-wavefront kernels where blocks allow (KVX_ONE_BATCH)
 };
 const Tuning& tuning();
 
