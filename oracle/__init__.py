@@ -21,9 +21,13 @@ from .kv_oracle import (  # noqa: F401
     MODE_UNPACK,
     buffer_order,
     pack,
+    pack_kv_first,
+    pack_split,
     reshape_and_cache,
     slot_mapping,
+    split_block,
     unpack,
     unpack_block,
+    unpack_kv_first,
     xfer_list,
 )

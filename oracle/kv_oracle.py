@@ -276,3 +276,113 @@ def unpack(src_buffers: Sequence[np.ndarray], dst_caches: Sequence[np.ndarray],
             else:
                 out[l][d] = unpack_block([bufs[s][l, p] for s in range(S)], rows_per_block)
     return out, err
+
+
+# ---------------------------------------------------------------------------------------
+# f1 — kv-first caches: (K/V plane, blocks, block_size, heads, head_dim)
+# ---------------------------------------------------------------------------------------
+
+def _planes(cache: np.ndarray) -> np.ndarray:
+    """A kv-first layer cache viewed as [2][num_blocks][segment bytes] uint8."""
+    c = np.ascontiguousarray(cache)
+    return c.reshape(2, c.shape[1], -1).view(np.uint8)
+
+
+def pack_kv_first(layer_caches: Sequence[np.ndarray], src_tables: Sequence[np.ndarray]
+                  ) -> Tuple[np.ndarray, int]:
+    """Gather from kv-first caches. For each layer and each request r, the buffer holds the
+    request's blocks as the gather over the block axis returns them: every listed block's K
+    segment in table order, then every listed block's V segment. [nccl] §2.4
+    (extract_kv_from_layer indexes dimension 1 when the K/V dimension comes first); [v1] the
+    two "shape of layer i" layouts (reading: kv-first = (2, blocks, ...)).
+
+    Buffer layout: [L][sum over r of 2*n_r][segment bytes]; request r starts at segment
+    2*(blocks of earlier requests). Out-of-range ids are skipped (zeros) and raise
+    DEVERR_BLOCK_RANGE.
+    """
+    planes = [_planes(c) for c in layer_caches]
+    L = len(planes)
+    _, nb, seg = planes[0].shape
+    N = sum(len(t) for t in src_tables)
+    buf = np.zeros((L, 2 * N, seg), np.uint8)
+    err = 0
+    for l in range(L):
+        at = 0
+        for t in src_tables:
+            for kv in range(2):
+                for b in t:
+                    b = int(b)
+                    if 0 <= b < nb:
+                        buf[l, at] = planes[l][kv, b]
+                    else:
+                        err |= DEVERR_BLOCK_RANGE
+                    at += 1
+    return buf, err
+
+
+def unpack_kv_first(buf: np.ndarray, dst_caches: Sequence[np.ndarray],
+                    dst_tables: Sequence[np.ndarray]) -> Tuple[List[np.ndarray], int]:
+    """Inverse of pack_kv_first into the receiver's kv-first caches: request r's K segments
+    go to plane 0 of its destination blocks in table order, then its V segments to plane 1.
+    [nccl] §2.3 step 14 / §2.4 (inject_kv_into_layer). Unlisted blocks keep their bytes;
+    out-of-range destination ids are skipped and raise DEVERR_BLOCK_RANGE."""
+    out = [_planes(c).copy() for c in dst_caches]
+    L = len(out)
+    _, nb, seg = out[0].shape
+    N = sum(len(t) for t in dst_tables)
+    src = np.ascontiguousarray(buf).reshape(L, 2 * N, -1).view(np.uint8)
+    err = 0
+    for l in range(L):
+        at = 0
+        for t in dst_tables:
+            for kv in range(2):
+                for d in t:
+                    d = int(d)
+                    if 0 <= d < nb:
+                        out[l][kv, d] = src[l, at]
+                    else:
+                        err |= DEVERR_BLOCK_RANGE
+                    at += 1
+    return out, err
+
+
+# ---------------------------------------------------------------------------------------
+# f2 — sender-side head split (the inverse of the receiver's head merge)
+# ---------------------------------------------------------------------------------------
+
+def split_block(block: np.ndarray, num_dst: int, rows_per_block: int) -> List[np.ndarray]:
+    """Cut one full-head block into num_dst head shards: shard d's row k is the d-th of
+    num_dst equal pieces of the block's row k. [pd] §四 4.2 (TP heterogeneity). Reading:
+    receiver rank d owns heads [d*H/num_dst, (d+1)*H/num_dst)."""
+    b = np.ascontiguousarray(block).reshape(-1).view(np.uint8)
+    row = len(b) // rows_per_block
+    piece = row // num_dst
+    shards = [np.empty(rows_per_block * piece, np.uint8) for _ in range(num_dst)]
+    for k in range(rows_per_block):
+        for d in range(num_dst):
+            shards[d][k * piece:(k + 1) * piece] = b[k * row + d * piece:k * row + (d + 1) * piece]
+    return shards
+
+
+def pack_split(layer_caches: Sequence[np.ndarray], src_tables: Sequence[np.ndarray],
+               num_dst: int, rows_per_block: int) -> Tuple[List[np.ndarray], int]:
+    """Pack for num_dst receiving ranks that each own a head shard: buffer d is
+    [L][N][block_bytes/num_dst] in pack's order (layer, request, block-table order) and holds
+    shard d of every listed block (split_block). Out-of-range ids are skipped (zeros) and
+    raise DEVERR_BLOCK_RANGE."""
+    caches = [_as_block_bytes(c) for c in layer_caches]
+    L = len(caches)
+    nb, bb = caches[0].shape
+    order = buffer_order(src_tables)
+    N = len(order)
+    bufs = [np.zeros((L, N, bb // num_dst), np.uint8) for _ in range(num_dst)]
+    err = 0
+    for l in range(L):
+        for r, j, p in order:
+            b = int(src_tables[r][j])
+            if b < 0 or b >= nb:
+                err |= DEVERR_BLOCK_RANGE
+                continue
+            for d, shard in enumerate(split_block(caches[l][b], num_dst, rows_per_block)):
+                bufs[d][l, p] = shard
+    return bufs, err

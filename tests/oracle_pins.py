@@ -376,4 +376,131 @@ def pin_head_merge_one_source_is_plain(o):
     assert np.array_equal(a[0], b[0])
 
 
+
+
+# --------------------------------------------------------------------------- kv-first (f1)
+
+def _kv_first_tagged(num_blocks, seg):
+    c = np.zeros((2, num_blocks, seg), np.uint8)
+    for b in range(num_blocks):
+        c[0, b] = 10 + b
+        c[1, b] = 20 + b
+    return c
+
+
+def pin_kv_first_golden(o):
+    g = _golden("kv_first_hw7.json")
+    cache = _kv_first_tagged(g["num_blocks"], 16)
+    src = [np.array(t) for t in g["src_tables"]]
+    dst = [np.array(t) for t in g["dst_tables"]]
+    buf, err = o.pack_kv_first([cache], src)
+    assert err == 0 and buf.shape == (1, 6, 16)
+    assert buf[0, :, 0].tolist() == g["buffer_tags"] and np.all(buf == buf[:, :, :1])
+    out, err = o.unpack_kv_first(buf, [np.zeros_like(cache)], dst)
+    got = [[None if not out[0][kv, b].any() else int(out[0][kv, b][0]) for b in range(4)] for kv in range(2)]
+    assert err == 0 and got == g["dst_plane_tags_after_unpack"]
+
+
+def pin_kv_first_equals_block_axis_gather(o):
+    """Each request's slice equals numpy's gather along the block axis, layer[:, ids]."""
+    rng = np.random.default_rng(31)
+    caches = [W.random_words(rng, (2, 40, 4, 2, 8)) for _ in range(2)]
+    tables = [np.array([5, 6, 7, 1]), np.array([], dtype=np.int64), np.array([39, 0, 2])]
+    buf, err = o.pack_kv_first(caches, tables)
+    for l in range(2):
+        ref = np.concatenate([caches[l][:, t].reshape(-1) for t in tables]).view(np.uint8)
+        assert np.array_equal(buf[l].reshape(-1), ref)
+
+
+def pin_kv_first_element_loop(o):
+    rng = np.random.default_rng(32)
+    nb, bs, H, D = 9, 2, 2, 2
+    cache = W.random_words(rng, (2, nb, bs, H, D))
+    tables = [np.array([4, 1]), np.array([8])]
+    buf, _ = o.pack_kv_first([cache], tables)
+    b5 = buf.view(np.uint16).reshape(1, 6, bs, H, D)
+    seg_at = 0
+    for t in tables:
+        for kv in range(2):
+            for blk in t:
+                for tok in range(bs):
+                    for h in range(H):
+                        for e in range(D):
+                            assert b5[0, seg_at, tok, h, e] == cache[kv, blk, tok, h, e]
+                seg_at += 1
+
+
+def pin_kv_first_roundtrip(o):
+    rng = np.random.default_rng(33)
+    src = [W.random_words(rng, (2, 50, 64)) for _ in range(3)]
+    s_tab = [np.array([3, 4, 5, 9]), np.array([0]), np.array([], dtype=np.int64), np.array([49, 48])]
+    d_tab = [np.array([10, 11, 30, 31]), np.array([2]), np.array([], dtype=np.int64), np.array([0, 1])]
+    buf, _ = o.pack_kv_first(src, s_tab)
+    dst = [np.full((2, 50, 64), W.SENTINEL16, np.uint16) for _ in range(3)]
+    out, err = o.unpack_kv_first(buf, dst, d_tab)
+    listed = np.concatenate(d_tab).astype(int)
+    for l in range(3):
+        got = out[l].view(np.uint16).reshape(2, 50, 64)
+        assert np.array_equal(got[:, listed], src[l][:, np.concatenate(s_tab).astype(int)])
+        rest = np.setdiff1d(np.arange(50), listed)
+        assert np.all(got[:, rest] == W.SENTINEL16)
+
+
+def pin_kv_first_out_of_range(o):
+    cache = _kv_first_tagged(4, 16)
+    buf, err = o.pack_kv_first([cache], [np.array([1, 4]), np.array([-1])])
+    assert err == o.DEVERR_BLOCK_RANGE
+    assert buf[0, :, 0].tolist() == [11, 0, 21, 0, 0, 0]
+    out, err = o.unpack_kv_first(buf, [np.zeros_like(cache)], [np.array([2, -1]), np.array([7])])
+    assert err == o.DEVERR_BLOCK_RANGE
+    assert out[0][0, 2, 0] == 11 and out[0][1, 2, 0] == 21
+    assert out[0][:, [0, 1, 3]].sum() == 0
+
+
+# --------------------------------------------------------------------------- head split (f2)
+
+def pin_split_golden(o):
+    """HW6 read backwards: splitting the merged rows gives back the two senders' rows."""
+    g = _golden("head_merge_hw6.json")
+    full = np.array(g["expected"], np.uint16)
+    s0, s1 = o.split_block(full, 2, g["rows_per_block"])
+    assert s0.view(np.uint16).reshape(2, 2).tolist() == g["src0"]
+    assert s1.view(np.uint16).reshape(2, 2).tolist() == g["src1"]
+
+
+def pin_split_element_loop(o):
+    """Shard d holds heads [d*H/S, (d+1)*H/S) of every (token, K/V) row."""
+    for S in (2, 4):
+        rng = np.random.default_rng(40 + S)
+        nb, bs, H, D = 12, 2, 4, 2
+        caches = [W.random_words(rng, (nb, bs, 2, H, D)) for _ in range(2)]
+        tables = [np.array([3, 9, 10]), np.array([0])]
+        bufs, err = o.pack_split(caches, tables, S, rows_per_block=bs * 2)
+        assert err == 0
+        for d in range(S):
+            v = bufs[d].view(np.uint16).reshape(2, 4, bs, 2, H // S, D)
+            p = 0
+            for t in tables:
+                for blk in t:
+                    for l in range(2):
+                        for tok in range(bs):
+                            for kv in range(2):
+                                for h in range(H // S):
+                                    for e in range(D):
+                                        assert v[l, p, tok, kv, h, e] == caches[l][blk, tok, kv, d * (H // S) + h, e]
+                    p += 1
+
+
+def pin_split_then_merge_is_pack(o):
+    c = W.random_transfer(44, 2, 80, 4, 4, 8, [20, 0, 35, 6])
+    for S in (2, 4):
+        bufs, e1 = o.pack_split(c.src_caches, c.src_tables, S, rows_per_block=8)
+        merged, e2 = o.unpack(bufs, c.dst_caches, c.dst_tables, rows_per_block=8)
+        buf, _ = o.pack(c.src_caches, c.src_tables)
+        plain, _ = o.unpack([buf], c.dst_caches, c.dst_tables)
+        assert e1 == e2 == 0
+        for l in range(2):
+            assert np.array_equal(merged[l], plain[l])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -37,6 +37,15 @@ MUTANTS = [
     ("merge_transposed", "at = (k * S + s) * row_src", "at = (s * rows_per_block + k) * row_src"),
     ("merge_sources_swapped", "srcs[s][k * row_src:(k + 1) * row_src]", "srcs[S - 1 - s][k * row_src:(k + 1) * row_src]"),
     ("unpack_no_range_check", "if d < 0 or d >= nb:", "if d >= nb:"),
+    ("kv_first_interleaved", "            for kv in range(2):\n                for b in t:", "            for b in t:\n                for kv in range(2):"),
+    ("kv_first_planes_swapped", "buf[l, at] = planes[l][kv, b]", "buf[l, at] = planes[l][1 - kv, b]"),
+    ("kv_first_unpack_one_plane", "out[l][kv, d] = src[l, at]", "out[l][0, d] = src[l, at]"),
+    ("kv_first_no_range_check", "                    if 0 <= b < nb:\n                        buf[l, at]", "                    if b < nb:\n                        buf[l, at]"),
+    ("split_pieces_reversed", "b[k * row + d * piece:k * row + (d + 1) * piece]",
+     "b[k * row + (num_dst - 1 - d) * piece:k * row + (num_dst - d) * piece]"),
+    ("split_rows_transposed", "b[k * row + d * piece:k * row + (d + 1) * piece]",
+     "b[(d * rows_per_block + k) * piece:(d * rows_per_block + k + 1) * piece]"),
+    ("split_shards_misrouted", "                bufs[d][l, p] = shard", "                bufs[num_dst - 1 - d][l, p] = shard"),
 ]
 
 
