@@ -265,6 +265,18 @@ def main():
             med, mn = time_op(torch, fn, args.op_reps, flush)
             out_ops[n]["flushed_median_ms"] = round(med, 5)
             out_ops[n]["flushed_GB/s"] = round(copy_bytes / (med * 1e-3) / 1e9, 1)
+        # the same 48 allocations viewed as kv-first caches: (K plane, V plane) of 4 KiB segments
+        seg = BB // 2
+        for n, fn in (("pack_kv_first", lambda: K.kvx_pack_kv_first(src_bases, seg, nb * seg, nb, ro, xp, cp, N,
+                                                                     buf, err)),
+                      ("unpack_kv_first", lambda: K.kvx_unpack_kv_first(buf, dst_bases, seg, nb * seg, nb, ro, xu,
+                                                                         cu, N, err))):
+            med, mn = time_op(torch, fn, args.op_reps, flush)
+            out_ops[n] = {"workload": f"{case.name}, kv-first view: 48 x (2, {nb}, {seg} B)",
+                          "median_ms": round(med, 5), "GB/s": round(copy_bytes / (med * 1e-3) / 1e9, 1),
+                          "frac_of_peak": round(copy_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0, "device error flag raised"
         out_ops.update(other_workloads(torch, np, W, K, dev, flush, args.op_reps))
 
     cpu = None
@@ -320,6 +332,14 @@ def other_workloads(torch, np, W, K, dev, flush, reps):
     nbytes = 2 * L * N * BB
     out["merge_unpack_asym_tp"] = {
         "workload": "2 sources x 4 of 8 heads, 32 layers x 16 requests x 256 blocks -> [8192][16][K,V][8][128] bf16",
+        "bytes": nbytes, "median_ms": round(med, 4), "min_ms": round(mn, 4),
+        "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    # the sender side of the same shapes: full-head caches split into 2 head shards
+    xs, cs = K.new_xfer_list(N, dev)
+    K.kvx_build_xfer_list(ids, None, ro, K.MODE_PACK, xs, cs)
+    med, mn = time_op(torch, lambda: K.kvx_pack_split(bases, BB, nb, case.rows_per_block, xs, cs, N, srcs), reps, flush)
+    out["split_pack_asym_tp"] = {
+        "workload": "32 layers of [8192][16][K,V][8][128] bf16, 16 requests x 256 blocks -> 2 shards x 4 heads",
         "bytes": nbytes, "median_ms": round(med, 4), "min_ms": round(mn, 4),
         "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del srcs, dst

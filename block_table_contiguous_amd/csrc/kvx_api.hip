@@ -31,7 +31,7 @@ const char* kvx_status_string(kvx_status status) {
   return "kvx: unknown status";
 }
 
-int32_t kvx_abi_version(void) { return 1; }
+int32_t kvx_abi_version(void) { return 2; }
 
 kvx_status kvx_slot_mapping(const int32_t* block_table, int64_t num_reqs,
                             int64_t max_blocks_per_req, int64_t bt_row_stride,
@@ -131,9 +131,75 @@ kvx_status kvx_unpack(const void* const* send_bufs, int32_t num_src, void* const
     return from_hip(kvx::launch_copy_runs(false, layer_bases, num_layers, block_bytes,
                                           num_cache_blocks, xfers, xfer_count, total_blocks,
                                           const_cast<void*>(send_bufs[0]), err_flag, stream));
-  return from_hip(kvx::launch_merge_runs(send_bufs, num_src, layer_bases, num_layers, block_bytes,
-                                         num_cache_blocks, rows_per_block, xfers, xfer_count,
-                                         total_blocks, err_flag, stream));
+  return from_hip(kvx::launch_shards(false, const_cast<void* const*>(send_bufs), num_src, layer_bases,
+                                     num_layers, block_bytes, num_cache_blocks, rows_per_block,
+                                     xfers, xfer_count, total_blocks, err_flag, stream));
+}
+
+kvx_status kvx_pack_split(void* const* layer_bases, int32_t num_layers, int64_t block_bytes,
+                          int64_t num_cache_blocks, int32_t rows_per_block, const kvx_xfer* xfers,
+                          const int64_t* xfer_count, int64_t total_blocks, void* const* send_bufs,
+                          int32_t num_dst, int32_t* err_flag, hipStream_t stream) {
+  if (num_dst < 1 || num_dst > KVX_MAX_SOURCES || num_layers < 0 || block_bytes <= 0 ||
+      num_cache_blocks < 0 || total_blocks < 0 || total_blocks > kMaxBlocks || rows_per_block < 1)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (!mult16(block_bytes)) return KVX_ERR_MISALIGNED;
+  if (block_bytes % ((int64_t)rows_per_block * num_dst * 16) != 0) return KVX_ERR_INVALID_ARGUMENT;
+  if (num_layers == 0 || total_blocks == 0) return KVX_SUCCESS;
+  if (!send_bufs || !layer_bases || !xfers || !xfer_count) return KVX_ERR_INVALID_ARGUMENT;
+  for (int32_t d = 0; d < num_dst; ++d) {
+    if (!send_bufs[d]) return KVX_ERR_INVALID_ARGUMENT;
+    if (!aligned16(send_bufs[d])) return KVX_ERR_MISALIGNED;
+  }
+  return from_hip(kvx::launch_shards(true, send_bufs, num_dst, layer_bases, num_layers, block_bytes,
+                                     num_cache_blocks, rows_per_block, xfers, xfer_count,
+                                     total_blocks, err_flag, stream));
+}
+
+static kvx_status kv_first_checks(void* const* layer_bases, int32_t num_layers,
+                                  int64_t segment_bytes, int64_t plane_stride_bytes,
+                                  int64_t num_cache_blocks, const int64_t* req_offsets,
+                                  int32_t num_reqs, const kvx_xfer* xfers,
+                                  const int64_t* xfer_count, int64_t total_blocks,
+                                  const void* buffer) {
+  if (num_layers < 0 || segment_bytes <= 0 || plane_stride_bytes < 0 || num_cache_blocks < 0 ||
+      total_blocks < 0 || total_blocks > kMaxBlocks || num_reqs < 0)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (segment_bytes % 1024 != 0 || !mult16(plane_stride_bytes)) return KVX_ERR_MISALIGNED;
+  if (num_layers == 0 || total_blocks == 0) return KVX_SUCCESS;
+  if (num_reqs == 0 || !layer_bases || !req_offsets || !xfers || !xfer_count || !buffer)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (!aligned16(buffer)) return KVX_ERR_MISALIGNED;
+  return KVX_SUCCESS;
+}
+
+kvx_status kvx_pack_kv_first(void* const* layer_bases, int32_t num_layers, int64_t segment_bytes,
+                             int64_t plane_stride_bytes, int64_t num_cache_blocks,
+                             const int64_t* req_offsets, int32_t num_reqs, const kvx_xfer* xfers,
+                             const int64_t* xfer_count, int64_t total_blocks, void* send_buf,
+                             int32_t* err_flag, hipStream_t stream) {
+  const kvx_status st = kv_first_checks(layer_bases, num_layers, segment_bytes, plane_stride_bytes,
+                                        num_cache_blocks, req_offsets, num_reqs, xfers, xfer_count,
+                                        total_blocks, send_buf);
+  if (st != KVX_SUCCESS || num_layers == 0 || total_blocks == 0) return st;
+  return from_hip(kvx::launch_kv_first(true, layer_bases, num_layers, segment_bytes,
+                                       plane_stride_bytes, num_cache_blocks, req_offsets, num_reqs,
+                                       xfers, xfer_count, total_blocks, send_buf, err_flag, stream));
+}
+
+kvx_status kvx_unpack_kv_first(const void* send_buf, void* const* layer_bases, int32_t num_layers,
+                               int64_t segment_bytes, int64_t plane_stride_bytes,
+                               int64_t num_cache_blocks, const int64_t* req_offsets,
+                               int32_t num_reqs, const kvx_xfer* xfers, const int64_t* xfer_count,
+                               int64_t total_blocks, int32_t* err_flag, hipStream_t stream) {
+  const kvx_status st = kv_first_checks(layer_bases, num_layers, segment_bytes, plane_stride_bytes,
+                                        num_cache_blocks, req_offsets, num_reqs, xfers, xfer_count,
+                                        total_blocks, send_buf);
+  if (st != KVX_SUCCESS || num_layers == 0 || total_blocks == 0) return st;
+  return from_hip(kvx::launch_kv_first(false, layer_bases, num_layers, segment_bytes,
+                                       plane_stride_bytes, num_cache_blocks, req_offsets, num_reqs,
+                                       xfers, xfer_count, total_blocks, const_cast<void*>(send_buf),
+                                       err_flag, stream));
 }
 
 }  // extern "C"

@@ -488,36 +488,38 @@ __global__ __launch_bounds__(kCopyThreads) void copy_runs_kernel(RunCopyArgs a) 
 }
 
 // --------------------------------------------------------------------------------------
-// a6 — unpack merging head-split sources
+// a6 — head shards: merge (unpack from num_shards senders) and split (pack for num_shards
+// receivers). A full-head cache block is rows_per_block rows; shard d holds piece d of
+// every row, contiguously, in pack order.
 // --------------------------------------------------------------------------------------
 
-struct MergeArgs {
-  const char* src[KVX_MAX_SOURCES];
+struct ShardArgs {
+  char* shard[KVX_MAX_SOURCES];  // [L][N][block_bytes/num_shards] each
   const char* const* layer_bases;
   const kvx_xfer* xfers;
   const int64_t* xfer_count;
   int32_t* err;
-  int64_t block_bytes;       // destination block
+  int64_t block_bytes;  // full-head cache block
   int64_t num_cache_blocks;
   int64_t total_blocks;
-  int64_t row_src;           // bytes of one source row
+  int64_t row_piece;    // bytes of one shard's piece of a row
   int64_t blocks_per_wave;
   int64_t waves_per_layer;
   int64_t total_waves;
   int64_t num_wgs;
-  int32_t num_src;
+  int32_t num_shards;
   int32_t rows_per_block;
   int32_t num_layers;
   int32_t xcd_remap;
 };
 
-// Same work split as copy_runs_kernel. For each overlap of n blocks the destination is
-// n*rows_per_block rows of num_src*row_src bytes; source s supplies the s-th row_src piece of
-// every row from its own contiguous n*rows_per_block*row_src bytes. Per source the wavefront
-// streams the source rows in order (one 1 KiB instruction per row piece when row_src is
-// 1 KiB) and writes them at the destination row stride.
-template <bool NTL, bool NTS>
-__global__ __launch_bounds__(kCopyThreads) void merge_runs_kernel(MergeArgs a) {
+// Same work split as copy_runs_kernel. For each overlap of n blocks the cache side is
+// n*rows_per_block rows of num_shards*row_piece bytes, and shard d's side is its own
+// contiguous n*rows_per_block*row_piece bytes. Per shard the wavefront streams that shard's
+// rows in order and meets the cache at the full row stride. TO_BUFFER = split (cache ->
+// shards, ids from the run's source side); otherwise merge (shards -> cache).
+template <bool TO_BUFFER, bool NTL, bool NTS>
+__global__ __launch_bounds__(kCopyThreads) void shard_runs_kernel(ShardArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t wg = blockIdx.x;
   if (a.xcd_remap) wg = xcd_slice_order(wg, a.num_wgs);
@@ -528,13 +530,13 @@ __global__ __launch_bounds__(kCopyThreads) void merge_runs_kernel(MergeArgs a) {
   const int64_t N = a.total_blocks;
   const int64_t p0 = c * a.blocks_per_wave;
   const int64_t p1 = (p0 + a.blocks_per_wave < N) ? p0 + a.blocks_per_wave : N;
-  const int64_t S = a.num_src;
+  const int64_t S = a.num_shards;
   const int64_t BB = a.block_bytes;
   const int64_t BBs = BB / S;
-  const int64_t row_src = a.row_src;
-  const int64_t row_dst = row_src * S;
-  const int64_t vs = row_src / kVec;                  // vectors per source row
-  const int64_t M = (vs + kWave - 1) / kWave;         // instructions per source row
+  const int64_t piece = a.row_piece;
+  const int64_t row_full = piece * S;
+  const int64_t vs = piece / kVec;                    // vectors per piece
+  const int64_t M = (vs + kWave - 1) / kWave;         // instructions per piece
   int64_t count = *a.xfer_count;
   if (count > N) count = N;
   if (count <= 0) return;
@@ -551,19 +553,19 @@ __global__ __launch_bounds__(kCopyThreads) void merge_runs_kernel(MergeArgs a) {
     const int64_t re = rb + (int64_t)x.num_blocks;
     const int64_t hi = re < p1 ? re : p1;
     if (lo >= hi) continue;
-    const int64_t id0 = x.dst_block + (lo - rb);
+    const int64_t id0 = (TO_BUFFER ? x.src_block : x.dst_block) + (lo - rb);
     const int64_t id1 = id0 + (hi - lo);
     const int64_t v0 = id0 > 0 ? id0 : 0;
     const int64_t v1 = id1 < a.num_cache_blocks ? id1 : a.num_cache_blocks;
     if (v0 != id0 || v1 != id1) bad = true;
     if (v0 >= v1) continue;
     const int64_t bpos = lo + (v0 - id0);
-    char* dblk = cache + v0 * BB;
+    char* cblk = cache + v0 * BB;
     const int64_t rows = (v1 - v0) * a.rows_per_block;
     const int64_t steps = rows * M;
-    for (int64_t s = 0; s < S; ++s) {
-      const char* sblk = a.src[s] + (l * N + bpos) * BBs;
-      char* dcol = dblk + s * row_src;
+    for (int64_t d = 0; d < S; ++d) {
+      char* sblk = a.shard[d] + (l * N + bpos) * BBs;
+      char* ccol = cblk + d * piece;
       int64_t row = 0, m = 0;
       for (int64_t t0 = 0; t0 < steps; t0 += kCopyBatch) {
         const char* sp[kCopyBatch];
@@ -573,8 +575,10 @@ __global__ __launch_bounds__(kCopyThreads) void merge_runs_kernel(MergeArgs a) {
         for (int j = 0; j < kCopyBatch; ++j) {
           const int64_t xv = m * kWave + lane;
           act[j] = (t0 + j < steps) && (xv < vs);
-          sp[j] = sblk + row * row_src + xv * kVec;
-          dp[j] = dcol + row * row_dst + xv * kVec;
+          char* sh = sblk + row * piece + xv * kVec;
+          char* ca = ccol + row * row_full + xv * kVec;
+          sp[j] = TO_BUFFER ? ca : sh;
+          dp[j] = TO_BUFFER ? sh : ca;
           if (++m == M) { m = 0; ++row; }
         }
         u32x4 v[kCopyBatch];
@@ -669,12 +673,13 @@ __global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(RunCopyArgs a)
   if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_BLOCK_RANGE);
 }
 
-// Head merge when a source row is a multiple of 1 KiB. Wavefront w owns kUnitBytes of one
-// layer's destination bytes taken in buffer order (position q, then row, then source, then
-// byte); slot j is the 1 KiB piece at destination offset w_in of block q, which is bytes
-// [xo, xo + 1 KiB) of row `row` of source s. Counters step (xo, s, row, q) without divisions.
-template <bool NTL, bool NTS>
-__global__ __launch_bounds__(kCopyThreads) void merge_slots_kernel(MergeArgs a) {
+// Head shards when a row piece is a multiple of 1 KiB. Wavefront w owns kUnitBytes of one
+// layer's cache-side bytes taken in buffer order (position q, then row, then shard, then
+// byte); slot j is the 1 KiB at offset w_in of the cache block for position q, which is
+// bytes [xo, xo + 1 KiB) of row `row` of shard d. Counters step (xo, d, row, q) without
+// divisions. TO_BUFFER = split (cache -> shards), otherwise merge (shards -> cache).
+template <bool TO_BUFFER, bool NTL, bool NTS>
+__global__ __launch_bounds__(kCopyThreads) void shard_slots_kernel(ShardArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t wg = blockIdx.x;
   if (a.xcd_remap) wg = xcd_slice_order(wg, a.num_wgs);
@@ -683,11 +688,11 @@ __global__ __launch_bounds__(kCopyThreads) void merge_slots_kernel(MergeArgs a) 
   const int64_t l = w / a.waves_per_layer;
   const int64_t u = w - l * a.waves_per_layer;
   const int64_t N = a.total_blocks;
-  const int64_t S = a.num_src;
+  const int64_t S = a.num_shards;
   const int64_t BB = a.block_bytes;
   const int64_t BBs = BB / S;
-  const int64_t row_src = a.row_src;
-  const int64_t row_dst = row_src * S;
+  const int64_t piece = a.row_piece;
+  const int64_t row_full = piece * S;
   const int64_t layer_bytes = N * BB;
   const KVX_CONST kvx_xfer* xf = readonly(a.xfers);
   int64_t count = *readonly(a.xfer_count);
@@ -698,15 +703,15 @@ __global__ __launch_bounds__(kCopyThreads) void merge_slots_kernel(MergeArgs a) 
   const int64_t o0 = u * kUnitBytes;
   int64_t q = o0 / BB;
   int64_t w_in = o0 - q * BB;
-  int64_t row = w_in / row_dst;
-  int64_t rem = w_in - row * row_dst;
-  int64_t s = rem / row_src;
-  int64_t xo = rem - s * row_src;
+  int64_t row = w_in / row_full;
+  int64_t rem = w_in - row * row_full;
+  int64_t d = rem / piece;
+  int64_t xo = rem - d * piece;
   int64_t k = uniform(find_run(a.xfers, count, q, lane));
   if (k < 0) k = 0;
   Run x = load_run(xf, k);
-  // Idle slots load from the first KiB of source 0's layer slice (always in bounds).
-  const char* idle = a.src[0] + l * N * BBs;
+  // Idle slots load the first KiB of shard 0's layer slice (always in bounds).
+  const char* idle = a.shard[0] + l * N * BBs;
   const char* sp[kCopyBatch];
   char* dp[kCopyBatch];
   bool on[kCopyBatch];
@@ -720,10 +725,12 @@ __global__ __launch_bounds__(kCopyThreads) void merge_slots_kernel(MergeArgs a) 
     if (o < layer_bytes) {
       while (x.buf + x.n <= q && k + 1 < count) x = load_run(xf, ++k);
       if (q >= x.buf && q < x.buf + x.n) {
-        const int64_t id = x.dst + (q - x.buf);
+        const int64_t id = (TO_BUFFER ? x.src : x.dst) + (q - x.buf);
         if (id >= 0 && id < a.num_cache_blocks) {
-          sp[j] = a.src[s] + (l * N + q) * BBs + row * row_src + xo;
-          dp[j] = cache + id * BB + w_in;
+          char* sh = a.shard[d] + (l * N + q) * BBs + row * piece + xo;
+          char* ca = cache + id * BB + w_in;
+          sp[j] = TO_BUFFER ? ca : sh;
+          dp[j] = TO_BUFFER ? sh : ca;
           on[j] = true;
         } else {
           bad = true;
@@ -732,11 +739,158 @@ __global__ __launch_bounds__(kCopyThreads) void merge_slots_kernel(MergeArgs a) 
     }
     xo += kWaveBytes;
     w_in += kWaveBytes;
-    if (xo == row_src) {
+    if (xo == piece) {
       xo = 0;
-      if (++s == S) { s = 0; ++row; }
+      if (++d == S) { d = 0; ++row; }
     }
-    if (w_in == BB) { w_in = 0; row = 0; s = 0; xo = 0; ++q; }
+    if (w_in == BB) { w_in = 0; row = 0; d = 0; xo = 0; ++q; }
+  }
+  u32x4 v[kCopyBatch];
+#pragma unroll
+  for (int j = 0; j < kCopyBatch; ++j) v[j] = load16<NTL>(sp[j] + lane * kVec);
+#pragma unroll
+  for (int j = 0; j < kCopyBatch; ++j)
+    if (on[j]) store16<NTS>(dp[j] + lane * kVec, v[j]);
+  if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_BLOCK_RANGE);
+}
+
+// --------------------------------------------------------------------------------------
+// f1 — kv-first caches (K plane, then V plane): one-batch kernel
+// --------------------------------------------------------------------------------------
+
+struct KvFirstArgs {
+  const char* const* layer_bases;  // K plane base per layer; V plane at + plane_stride
+  char* buffer;                    // [L][2N][segment]
+  const kvx_xfer* xfers;
+  const int64_t* xfer_count;
+  const int64_t* req_offsets;      // [R+1]
+  int32_t* err;
+  int64_t segment_bytes;           // one block in one plane (a multiple of 1 KiB)
+  int64_t plane_stride;
+  int64_t num_cache_blocks;
+  int64_t total_blocks;
+  int64_t waves_per_layer;
+  int64_t total_waves;
+  int64_t num_wgs;
+  int32_t num_reqs;
+  int32_t num_layers;
+  int32_t xcd_remap;
+};
+
+// Largest r in [0, R) with 2*ro[r] <= g: the request owning buffer segment g (empty
+// requests are skipped because the largest such r is taken). 64-way search as find_run.
+__device__ __forceinline__ int64_t find_segment_request(const int64_t* __restrict__ ro, int64_t R,
+                                                        int64_t g, int lane) {
+  int64_t lo = 0, hi = R;
+  while (hi - lo > 1) {
+    const int64_t step = (hi - lo + kWave - 1) / kWave;
+    const int64_t idx = lo + (int64_t)lane * step;
+    const bool pred = idx < hi && 2 * ro[idx] <= g;
+    const uint64_t m = __ballot(pred);
+    if (m == 0) return lo;
+    const int64_t j = 63 - __builtin_clzll(m);
+    lo = lo + j * step;
+    hi = (lo + step < hi) ? lo + step : hi;
+  }
+  return lo;
+}
+
+// The buffer slice of layer l is, per request r, its K segments in table order, then its V
+// segments (what a gather along the block axis of a (2, blocks, ...) tensor returns).
+// Wavefront w owns kUnitBytes of that slice: slot j is 1 KiB of segment g, which belongs to
+// request r, plane `plane` and table index jj, i.e. position p = cum_r + jj. Runs never
+// span requests, so p walks the runs of request r once per plane; the wavefront keeps the
+// index of the request's first run to restart the walk for the V plane.
+template <bool TO_BUFFER, bool NTL, bool NTS>
+__global__ __launch_bounds__(kCopyThreads) void kv_first_kernel(KvFirstArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t wg = blockIdx.x;
+  if (a.xcd_remap) wg = xcd_slice_order(wg, a.num_wgs);
+  const int64_t w = uniform(wg * kCopyWavesPerWg + (threadIdx.x / kWave));
+  if (w >= a.total_waves) return;
+  const int64_t l = w / a.waves_per_layer;
+  const int64_t u = w - l * a.waves_per_layer;
+  const int64_t N = a.total_blocks;
+  const int64_t R = a.num_reqs;
+  const int64_t SEG = a.segment_bytes;
+  const int64_t layer_bytes = 2 * N * SEG;
+  const KVX_CONST kvx_xfer* xf = readonly(a.xfers);
+  const KVX_CONST int64_t* ro = readonly(a.req_offsets);
+  int64_t count = *readonly(a.xfer_count);
+  if (count > N) count = N;
+  if (count <= 0) return;
+  char* cache = const_cast<char*>(*readonly(a.layer_bases + l));
+  char* buf = a.buffer + l * layer_bytes;
+
+  const int64_t o0 = u * kUnitBytes;
+  int64_t g = o0 / SEG;
+  int64_t in_seg = o0 - g * SEG;
+  int64_t r = uniform(find_segment_request(a.req_offsets, R, g, lane));
+  int64_t cum = ro[r];
+  int64_t n_r = ro[r + 1] - cum;
+  int64_t local = g - 2 * cum;
+  int64_t plane = local >= n_r ? 1 : 0;
+  int64_t jj = local - plane * n_r;
+  int64_t p = cum + jj;
+  int64_t k_first = uniform(find_run(a.xfers, count, cum, lane));
+  if (k_first < 0) k_first = 0;
+  int64_t k = uniform(find_run(a.xfers, count, p, lane));
+  if (k < 0) k = 0;
+  Run x = load_run(xf, k);
+  const char* idle = buf + o0;
+  const char* sp[kCopyBatch];
+  char* dp[kCopyBatch];
+  bool on[kCopyBatch];
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < kCopyBatch; ++j) {
+    const int64_t o = o0 + (int64_t)j * kWaveBytes;
+    on[j] = false;
+    sp[j] = idle;
+    dp[j] = nullptr;
+    if (o < layer_bytes && jj < n_r) {
+      while (x.buf + x.n <= p && k + 1 < count) x = load_run(xf, ++k);
+      if (p >= x.buf && p < x.buf + x.n) {
+        const int64_t id = (TO_BUFFER ? x.src : x.dst) + (p - x.buf);
+        if (id >= 0 && id < a.num_cache_blocks) {
+          char* c = cache + plane * a.plane_stride + id * SEG + in_seg;
+          char* b = buf + o;
+          sp[j] = TO_BUFFER ? c : b;
+          dp[j] = TO_BUFFER ? b : c;
+          on[j] = true;
+        } else {
+          bad = true;
+        }
+      }
+    }
+    in_seg += kWaveBytes;
+    if (in_seg == SEG) {
+      in_seg = 0;
+      ++jj;
+      ++p;
+      if (jj == n_r) {
+        if (plane == 0) {  // V plane of the same request: restart its runs
+          plane = 1;
+          jj = 0;
+          p = cum;
+          k = k_first;
+          x = load_run(xf, k);
+        } else {           // next non-empty request: its first run follows this one
+          while (r + 1 < R && ro[r + 2] == ro[r + 1]) ++r;
+          if (r + 1 < R) {
+            ++r;
+            cum = ro[r];
+            n_r = ro[r + 1] - cum;
+            plane = 0;
+            jj = 0;
+            p = cum;
+            if (k + 1 < count) ++k;
+            k_first = k;
+            x = load_run(xf, k);
+          }
+        }
+      }
+    }
   }
   u32x4 v[kCopyBatch];
 #pragma unroll
@@ -855,13 +1009,13 @@ hipError_t launch_copy_runs(bool to_buffer, void* const* layer_bases, int32_t nu
   return hipGetLastError();
 }
 
-hipError_t launch_merge_runs(const void* const* srcs, int32_t num_src, void* const* layer_bases,
-                             int32_t num_layers, int64_t block_bytes, int64_t num_cache_blocks,
-                             int32_t rows_per_block, const kvx_xfer* xfers,
-                             const int64_t* xfer_count, int64_t total_blocks, int32_t* err,
-                             hipStream_t stream) {
-  MergeArgs a;
-  for (int i = 0; i < KVX_MAX_SOURCES; ++i) a.src[i] = i < num_src ? (const char*)srcs[i] : nullptr;
+hipError_t launch_shards(bool to_buffer, void* const* shards, int32_t num_shards,
+                         void* const* layer_bases, int32_t num_layers, int64_t block_bytes,
+                         int64_t num_cache_blocks, int32_t rows_per_block, const kvx_xfer* xfers,
+                         const int64_t* xfer_count, int64_t total_blocks, int32_t* err,
+                         hipStream_t stream) {
+  ShardArgs a;
+  for (int i = 0; i < KVX_MAX_SOURCES; ++i) a.shard[i] = i < num_shards ? (char*)shards[i] : nullptr;
   a.layer_bases = (const char* const*)layer_bases;
   a.xfers = xfers;
   a.xfer_count = xfer_count;
@@ -869,33 +1023,74 @@ hipError_t launch_merge_runs(const void* const* srcs, int32_t num_src, void* con
   a.block_bytes = block_bytes;
   a.num_cache_blocks = num_cache_blocks;
   a.total_blocks = total_blocks;
-  a.row_src = block_bytes / ((int64_t)rows_per_block * num_src);
-  const bool slots = use_slots(a.row_src % kWaveBytes == 0, num_layers, total_blocks * block_bytes);
+  a.row_piece = block_bytes / ((int64_t)rows_per_block * num_shards);
+  const CopyTuning& ct = to_buffer ? tuning().pack : tuning().merge;
+  const bool slots = use_slots(a.row_piece % kWaveBytes == 0, num_layers, total_blocks * block_bytes);
   if (slots) {
     a.blocks_per_wave = 0;
     a.waves_per_layer = ceil_div(total_blocks * block_bytes, kUnitBytes);
   } else {
-    a.blocks_per_wave = blocks_per_wave_for(tuning().merge.wave_bytes, block_bytes, num_layers,
-                                            total_blocks);
+    a.blocks_per_wave = blocks_per_wave_for(ct.wave_bytes, block_bytes, num_layers, total_blocks);
     a.waves_per_layer = ceil_div(total_blocks, a.blocks_per_wave);
   }
   a.total_waves = a.waves_per_layer * num_layers;
   a.num_wgs = ceil_div(a.total_waves, kCopyWavesPerWg);
-  a.num_src = num_src;
+  a.num_shards = num_shards;
   a.rows_per_block = rows_per_block;
   a.num_layers = num_layers;
   a.xcd_remap = tuning().xcd_remap;
   const unsigned grid = (unsigned)a.num_wgs;
-#define KVX_MERGE_LAUNCH(NTL, NTS)                                                  \
-  if (slots) merge_slots_kernel<NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);   \
-  else merge_runs_kernel<NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
-  switch (tuning().merge.nt_mode & 3) {
-    case 0: KVX_MERGE_LAUNCH(false, false) break;
-    case 1: KVX_MERGE_LAUNCH(true, false) break;
-    case 2: KVX_MERGE_LAUNCH(false, true) break;
-    default: KVX_MERGE_LAUNCH(true, true) break;
+#define KVX_SHARD_LAUNCH(TB, NTL, NTS)                                                   \
+  if (slots) shard_slots_kernel<TB, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);    \
+  else shard_runs_kernel<TB, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
+#define KVX_SHARD_POLICY(TB)                            \
+  switch (ct.nt_mode & 3) {                             \
+    case 0: KVX_SHARD_LAUNCH(TB, false, false) break;   \
+    case 1: KVX_SHARD_LAUNCH(TB, true, false) break;    \
+    case 2: KVX_SHARD_LAUNCH(TB, false, true) break;    \
+    default: KVX_SHARD_LAUNCH(TB, true, true) break;    \
   }
-#undef KVX_MERGE_LAUNCH
+  if (to_buffer) { KVX_SHARD_POLICY(true) }
+  else { KVX_SHARD_POLICY(false) }
+#undef KVX_SHARD_POLICY
+#undef KVX_SHARD_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_first(bool to_buffer, void* const* layer_bases, int32_t num_layers,
+                           int64_t segment_bytes, int64_t plane_stride, int64_t num_cache_blocks,
+                           const int64_t* req_offsets, int32_t num_reqs, const kvx_xfer* xfers,
+                           const int64_t* xfer_count, int64_t total_blocks, void* buffer,
+                           int32_t* err, hipStream_t stream) {
+  KvFirstArgs a;
+  a.layer_bases = (const char* const*)layer_bases;
+  a.buffer = (char*)buffer;
+  a.xfers = xfers;
+  a.xfer_count = xfer_count;
+  a.req_offsets = req_offsets;
+  a.err = err;
+  a.segment_bytes = segment_bytes;
+  a.plane_stride = plane_stride;
+  a.num_cache_blocks = num_cache_blocks;
+  a.total_blocks = total_blocks;
+  a.waves_per_layer = ceil_div(2 * total_blocks * segment_bytes, kUnitBytes);
+  a.total_waves = a.waves_per_layer * num_layers;
+  a.num_wgs = ceil_div(a.total_waves, kCopyWavesPerWg);
+  a.num_reqs = num_reqs;
+  a.num_layers = num_layers;
+  a.xcd_remap = tuning().xcd_remap;
+  const unsigned grid = (unsigned)a.num_wgs;
+  const int nt = (to_buffer ? tuning().pack : tuning().unpack).nt_mode & 3;
+#define KVX_KVF_LAUNCH(TB)                                                                       \
+  switch (nt) {                                                                                  \
+    case 0: kv_first_kernel<TB, false, false><<<grid, kCopyThreads, 0, stream>>>(a); break;      \
+    case 1: kv_first_kernel<TB, true, false><<<grid, kCopyThreads, 0, stream>>>(a); break;       \
+    case 2: kv_first_kernel<TB, false, true><<<grid, kCopyThreads, 0, stream>>>(a); break;       \
+    default: kv_first_kernel<TB, true, true><<<grid, kCopyThreads, 0, stream>>>(a); break;       \
+  }
+  if (to_buffer) { KVX_KVF_LAUNCH(true) }
+  else { KVX_KVF_LAUNCH(false) }
+#undef KVX_KVF_LAUNCH
   return hipGetLastError();
 }
 

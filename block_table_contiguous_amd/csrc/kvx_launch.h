@@ -47,11 +47,18 @@ hipError_t launch_copy_runs(bool to_buffer, void* const* layer_bases, int32_t nu
                             const int64_t* xfer_count, int64_t total_blocks, void* buffer,
                             int32_t* err, hipStream_t stream);
 
-// unpack merging num_src >= 2 head-split sources
-hipError_t launch_merge_runs(const void* const* srcs, int32_t num_src, void* const* layer_bases,
-                             int32_t num_layers, int64_t block_bytes, int64_t num_cache_blocks,
-                             int32_t rows_per_block, const kvx_xfer* xfers,
-                             const int64_t* xfer_count, int64_t total_blocks, int32_t* err,
-                             hipStream_t stream);
+// head shards: split (to_buffer: cache -> num_shards buffers) or merge (buffers -> cache)
+hipError_t launch_shards(bool to_buffer, void* const* shards, int32_t num_shards,
+                         void* const* layer_bases, int32_t num_layers, int64_t block_bytes,
+                         int64_t num_cache_blocks, int32_t rows_per_block, const kvx_xfer* xfers,
+                         const int64_t* xfer_count, int64_t total_blocks, int32_t* err,
+                         hipStream_t stream);
+
+// kv-first caches (K plane, V plane at + plane_stride); segment_bytes a multiple of 1 KiB
+hipError_t launch_kv_first(bool to_buffer, void* const* layer_bases, int32_t num_layers,
+                           int64_t segment_bytes, int64_t plane_stride, int64_t num_cache_blocks,
+                           const int64_t* req_offsets, int32_t num_reqs, const kvx_xfer* xfers,
+                           const int64_t* xfer_count, int64_t total_blocks, void* buffer,
+                           int32_t* err, hipStream_t stream);
 
 }  // namespace kvx

@@ -50,6 +50,9 @@ SIGNATURES = {
     "kvx_build_xfer_list": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I32, _P, _I64, _P, _P, _P]),
     "kvx_pack": (ctypes.c_int, [_P, _I32, _I64, _I64, _P, _P, _I64, _P, _P, _P]),
     "kvx_unpack": (ctypes.c_int, [_P, _I32, _P, _I32, _I64, _I64, _I32, _P, _P, _I64, _P, _P]),
+    "kvx_pack_split": (ctypes.c_int, [_P, _I32, _I64, _I64, _I32, _P, _P, _I64, _P, _I32, _P, _P]),
+    "kvx_pack_kv_first": (ctypes.c_int, [_P, _I32, _I64, _I64, _I64, _P, _I32, _P, _P, _I64, _P, _P, _P]),
+    "kvx_unpack_kv_first": (ctypes.c_int, [_P, _P, _I32, _I64, _I64, _I64, _P, _I32, _P, _P, _I64, _P, _P]),
 }
 
 
@@ -279,3 +282,61 @@ def kvx_unpack(send_bufs: Sequence, layer_bases, block_bytes: int, num_cache_blo
                           int(rows_per_block), _ptr(xfers), _ptr(xfer_count), int(total_blocks),
                           _ptr(err_flag), _stream(stream))
     _check("kvx_unpack", st)
+
+
+def kvx_pack_split(layer_bases, block_bytes: int, num_cache_blocks: int, rows_per_block: int,
+                   xfers, xfer_count, total_blocks: int, send_bufs: Sequence, err_flag=None,
+                   stream=None):
+    """Pack for num_dst receivers that each own a head shard: send_bufs[d] gets piece d of
+    every row of every listed block (the inverse of kvx_unpack's merge)."""
+    import torch
+
+    _want(layer_bases, torch.int64, "layer_bases")
+    L = layer_bases.numel()
+    D = len(send_bufs)
+    if not 1 <= D <= MAX_SOURCES:
+        raise ValueError(f"kvx: 1..{MAX_SOURCES} send buffers")
+    for b in send_bufs:
+        if b.numel() * b.element_size() < L * total_blocks * (block_bytes // D):
+            raise ValueError("kvx: a send buffer is smaller than num_layers * total_blocks * block_bytes/num_dst")
+    arr = (ctypes.c_void_p * D)(*[_ptr(b) for b in send_bufs])
+    st = _F["kvx_pack_split"](_ptr(layer_bases), L, int(block_bytes), int(num_cache_blocks),
+                              int(rows_per_block), _ptr(xfers), _ptr(xfer_count), int(total_blocks), arr, D,
+                              _ptr(err_flag), _stream(stream))
+    _check("kvx_pack_split", st)
+
+
+def kvx_pack_kv_first(layer_bases, segment_bytes: int, plane_stride_bytes: int, num_cache_blocks: int,
+                      req_offsets, xfers, xfer_count, total_blocks: int, send_buf, err_flag=None,
+                      stream=None):
+    """Pack from kv-first caches: per layer and request, the K segments then the V segments."""
+    import torch
+
+    _want(layer_bases, torch.int64, "layer_bases")
+    _want(req_offsets, torch.int64, "req_offsets")
+    L = layer_bases.numel()
+    if send_buf.numel() * send_buf.element_size() < L * 2 * total_blocks * segment_bytes:
+        raise ValueError("kvx: send_buf smaller than num_layers * 2 * total_blocks * segment_bytes")
+    st = _F["kvx_pack_kv_first"](_ptr(layer_bases), L, int(segment_bytes), int(plane_stride_bytes),
+                                 int(num_cache_blocks), _ptr(req_offsets), req_offsets.numel() - 1,
+                                 _ptr(xfers), _ptr(xfer_count), int(total_blocks), _ptr(send_buf),
+                                 _ptr(err_flag), _stream(stream))
+    _check("kvx_pack_kv_first", st)
+
+
+def kvx_unpack_kv_first(send_buf, layer_bases, segment_bytes: int, plane_stride_bytes: int,
+                        num_cache_blocks: int, req_offsets, xfers, xfer_count, total_blocks: int,
+                        err_flag=None, stream=None):
+    """Scatter a kv-first buffer (per request: K segments, then V segments) into kv-first caches."""
+    import torch
+
+    _want(layer_bases, torch.int64, "layer_bases")
+    _want(req_offsets, torch.int64, "req_offsets")
+    L = layer_bases.numel()
+    if send_buf.numel() * send_buf.element_size() < L * 2 * total_blocks * segment_bytes:
+        raise ValueError("kvx: send_buf smaller than num_layers * 2 * total_blocks * segment_bytes")
+    st = _F["kvx_unpack_kv_first"](_ptr(send_buf), _ptr(layer_bases), L, int(segment_bytes),
+                                   int(plane_stride_bytes), int(num_cache_blocks), _ptr(req_offsets),
+                                   req_offsets.numel() - 1, _ptr(xfers), _ptr(xfer_count), int(total_blocks),
+                                   _ptr(err_flag), _stream(stream))
+    _check("kvx_unpack_kv_first", st)

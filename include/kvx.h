@@ -212,6 +212,54 @@ kvx_status kvx_unpack(const void* const* send_bufs, int32_t num_src, void* const
                       const int64_t* xfer_count, int64_t total_blocks, int32_t* err_flag,
                       hipStream_t stream);
 
+/*
+ * kvx_pack_split — sender-side head split for an asymmetric TP transfer where the receiver
+ * runs num_dst ranks ("vLLM PD 分离" §四 4.2, TP heterogeneity): the inverse of kvx_unpack's
+ * merge. Every full-head cache block is rows_per_block rows (block_size*2 for the
+ * [tokens][K,V][heads][head_dim] block); receiver d owns heads [d*H/num_dst, (d+1)*H/num_dst),
+ * i.e. piece d of each row. Buffer d is [num_layers][total_blocks][block_bytes/num_dst] in
+ * pack's order and holds piece d of every row of every listed block:
+ *     send_bufs[d][l][p] row k = bytes [d*piece, (d+1)*piece) of row k of the block that
+ *     kvx_pack would put at (l, p).
+ *   send_bufs     [host] array [num_dst] of device pointers, 1 <= num_dst <= KVX_MAX_SOURCES.
+ *   block_bytes must be a multiple of rows_per_block*num_dst*16. Runs: KVX_MODE_PACK or
+ *   KVX_MODE_DIRECT. Errors and range handling as kvx_pack.
+ */
+kvx_status kvx_pack_split(void* const* layer_bases, int32_t num_layers, int64_t block_bytes,
+                          int64_t num_cache_blocks, int32_t rows_per_block, const kvx_xfer* xfers,
+                          const int64_t* xfer_count, int64_t total_blocks, void* const* send_bufs,
+                          int32_t num_dst, int32_t* err_flag, hipStream_t stream);
+
+/*
+ * kvx_pack_kv_first / kvx_unpack_kv_first — the same transfer for kv-first caches, whose
+ * layer tensor is (K/V plane, blocks, block_size, heads, head_dim) ("vllm v1 调度逻辑 和
+ * distributed 分布式原理", "shape of layer i"; "0. vllm 如何使用 nccl 传输 kv cache" §2.4,
+ * which gathers along dimension 1 when the K/V dimension comes first).
+ *   A block is one segment_bytes segment in each plane: block b's K segment starts at
+ *   base + b*segment_bytes and its V segment at base + plane_stride_bytes + b*segment_bytes
+ *   (plane_stride_bytes = num_cache_blocks*segment_bytes for a contiguous tensor).
+ *   Buffer layout: [num_layers][2*total_blocks][segment_bytes]; in each layer, request r's
+ *   part starts at segment 2*req_offsets[r] and is its K segments in block-table order, then
+ *   its V segments — exactly what gathering the layer tensor along the block axis with the
+ *   request's block ids returns, one contiguous tensor per (request, layer).
+ *   req_offsets   int64 [num_reqs+1], the CSR the run list was built from.
+ *   segment_bytes must be a multiple of 1024 (KVX_ERR_MISALIGNED otherwise): true for any
+ *   16-token block with heads*head_dim a multiple of 32 at 2 bytes per element.
+ *   Runs: pack needs KVX_MODE_PACK or KVX_MODE_DIRECT; unpack KVX_MODE_UNPACK or
+ *   KVX_MODE_DIRECT. Out-of-range ids are skipped and raise KVX_DEVERR_BLOCK_RANGE.
+ */
+kvx_status kvx_pack_kv_first(void* const* layer_bases, int32_t num_layers, int64_t segment_bytes,
+                             int64_t plane_stride_bytes, int64_t num_cache_blocks,
+                             const int64_t* req_offsets, int32_t num_reqs, const kvx_xfer* xfers,
+                             const int64_t* xfer_count, int64_t total_blocks, void* send_buf,
+                             int32_t* err_flag, hipStream_t stream);
+
+kvx_status kvx_unpack_kv_first(const void* send_buf, void* const* layer_bases, int32_t num_layers,
+                               int64_t segment_bytes, int64_t plane_stride_bytes,
+                               int64_t num_cache_blocks, const int64_t* req_offsets,
+                               int32_t num_reqs, const kvx_xfer* xfers, const int64_t* xfer_count,
+                               int64_t total_blocks, int32_t* err_flag, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "kvx_abi_version", "kvx_build_xfer_list", "kvx_pack", "kvx_reshape_and_cache",
-        "kvx_slot_mapping", "kvx_status_string", "kvx_unpack"])
+        "kvx_slot_mapping", "kvx_status_string", "kvx_unpack", "kvx_pack_split",
+        "kvx_pack_kv_first", "kvx_unpack_kv_first"])
 
 
 def test_every_declared_symbol_is_exported(kvx):
@@ -39,7 +40,7 @@ def test_status_strings(kvx):
         s = kvx.kvx_status_string(code)
         assert s.startswith("kvx: ")
     assert "unknown" in kvx.kvx_status_string(99)
-    assert kvx.kvx_abi_version() == 1
+    assert kvx.kvx_abi_version() == 2
 
 
 def test_xfer_struct_size(kvx):
@@ -127,3 +128,28 @@ def test_slot_and_reshape_validation(kvx):
     assert rc(row=2040) == kvx.KVX_ERR_MISALIGNED
     assert rc(kst=2056) == kvx.KVX_ERR_MISALIGNED
     assert rc(T=0) == kvx.KVX_SUCCESS
+
+
+def test_split_and_kv_first_validation(kvx):
+    def split(D=2, bufs=(P, P), L=2, bb=65536, nb=100, rows=32, x=P, cnt=P, n=10):
+        arr = (ctypes.c_void_p * max(len(bufs), 1))(*bufs) if bufs is not None else None
+        return call(kvx, "kvx_pack_split", P, L, bb, nb, rows, x, cnt, n, arr, D, None, None)
+    assert split(D=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert split(D=9, bufs=(P,) * 9) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert split(rows=3) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert split(bufs=(P, None)) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert split(bufs=(P, P + 8)) == kvx.KVX_ERR_MISALIGNED
+    assert split(n=0) == kvx.KVX_SUCCESS
+
+    def kvf(fn, seg=4096, plane=4096 * 100, nb=100, ro=P, R=2, x=P, cnt=P, n=10, buf=P):
+        if fn == "kvx_pack_kv_first":
+            return call(kvx, fn, P, 2, seg, plane, nb, ro, R, x, cnt, n, buf, None, None)
+        return call(kvx, fn, buf, P, 2, seg, plane, nb, ro, R, x, cnt, n, None, None)
+    for fn in ("kvx_pack_kv_first", "kvx_unpack_kv_first"):
+        assert kvf(fn, seg=512) == kvx.KVX_ERR_MISALIGNED
+        assert kvf(fn, plane=8) == kvx.KVX_ERR_MISALIGNED
+        assert kvf(fn, seg=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+        assert kvf(fn, ro=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+        assert kvf(fn, R=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+        assert kvf(fn, buf=P + 16 + 8) == kvx.KVX_ERR_MISALIGNED
+        assert kvf(fn, n=0) == kvx.KVX_SUCCESS

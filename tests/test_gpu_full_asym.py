@@ -53,3 +53,41 @@ def test_asym_tp_full():
         want = O.unpack_block([host_bytes(t[l, p]) for t in srcs], case.rows_per_block)
         assert np.array_equal(host_bytes(dst[l][d_id]), want), (l, p, d_id)
     log("asym: sampled blocks identical")
+
+
+def test_asym_tp_split_full():
+    """The sender side of the same transfer with the roles reversed: 32 full-head
+    [8192][16][K,V][8][128] caches split into 2 head shards of 16 x 256 listed blocks."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    K = kvx()
+    case = W.asym_tp()
+    L, N, S = case.dst_spec.num_layers, case.total_blocks, case.num_src
+    BB, nb = case.dst_spec.block_bytes, case.dst_spec.num_blocks
+    BBs = BB // S
+    full = [W.fill_device_random_(torch.empty((nb, BB), dtype=torch.uint8, device=DEV), 900 + l)
+            for l in range(L)]
+    shards = [torch.zeros((L, N, BBs), dtype=torch.uint8, device=DEV) for _ in range(S)]
+    ids, ro = K.flatten_tables(case.dst_tables, DEV)
+    x, c = K.new_xfer_list(N, DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    K.kvx_build_xfer_list(ids, None, ro, K.MODE_PACK, x, c, err)
+    K.kvx_pack_split(K.layer_base_table(full), BB, nb, case.rows_per_block, x, c, N, shards, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for l in (0, L - 1):
+        exp, e = O.pack_split([host_bytes(full[l]).reshape(nb, BB)], case.dst_tables, S, case.rows_per_block)
+        assert e == 0
+        for d in range(S):
+            assert np.array_equal(host_bytes(shards[d][l]).reshape(N, BBs), exp[d][0]), f"layer {l} shard {d}"
+        log(f"split: layer {l} identical")
+    order = O.buffer_order(case.dst_tables)
+    rng = np.random.default_rng(11)
+    for _ in range(384):
+        l = int(rng.integers(L))
+        r, j, p = order[int(rng.integers(N))]
+        blk = int(case.dst_tables[r][j])
+        want = O.split_block(host_bytes(full[l][blk]), S, case.rows_per_block)
+        for d in range(S):
+            assert np.array_equal(host_bytes(shards[d][l, p]), want[d]), (l, p, d)
+    log("split: sampled blocks identical")
