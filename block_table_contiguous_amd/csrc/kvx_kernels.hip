@@ -37,6 +37,7 @@ const Tuning& tuning() {
       {env_i64("KVX_WAVE_BYTES_MERGE", 64 * 1024), (int)env_i64("KVX_NT_MERGE", 3)},
       (int)env_i64("KVX_XCD_REMAP", 1),
       (int)env_i64("KVX_ONE_BATCH", 1),
+      (int)env_i64("KVX_NT_WRITE", 1),
   };
   return t;
 }
@@ -74,6 +75,14 @@ constexpr int kWave = 64;
 constexpr int kVec = 16;                 // bytes per lane access
 constexpr int kWaveBytes = kWave * kVec; // bytes per wavefront instruction
 constexpr int kNumXcd = 8;               // MI355X: 8 XCDs, workgroups dealt round-robin
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyWavesPerWg = kCopyThreads / kWave;
+#ifndef KVX_COPY_BATCH
+#define KVX_COPY_BATCH 8
+#endif
+// 1 KiB wavefront loads a lane issues before its stores (8 -> 8 KiB in flight per wavefront)
+constexpr int kCopyBatch = KVX_COPY_BATCH;
 
 template <bool NT>
 __device__ __forceinline__ u32x4 load16(const char* p) {
@@ -259,6 +268,95 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
+struct WriteArgs {
+  const char* key;
+  const char* value;
+  const int64_t* slots;
+  char* cache;
+  int32_t* err;
+  int64_t key_stride, value_stride;
+  int64_t num_tokens, row_bytes, num_blocks;
+  int64_t block_stride, token_stride, kv_stride;
+  int64_t total_slots;  // num_tokens * 2 * row KiB
+  int32_t block_size;
+};
+
+// New-token write when a row is a multiple of 1 KiB. The (token, K/V, KiB of row) sequence
+// is cut into 1 KiB slots and wavefront w owns slots [8w, 8w + 8): a 2 KiB row puts two
+// tokens in one wavefront, an 8 KiB row spreads a token over two. The row loads do not
+// depend on the slot mapping, so all of them are in flight before the (scalar) slot loads;
+// then each slot's destination is formed and the stores go out, one batch per wavefront.
+template <bool NTL, bool NTS>
+__global__ __launch_bounds__(256) void write_slots_kernel(WriteArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t w = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
+  const int64_t s0 = w * kCopyBatch;
+  if (s0 >= a.total_slots) return;
+  const int64_t row_kib = a.row_bytes / kWaveBytes;
+  const int64_t per_tok = 2 * row_kib;
+  int64_t t = s0 / per_tok;
+  const int64_t within = s0 - t * per_tok;
+  int64_t kv = within / row_kib;
+  int64_t piece = within - kv * row_kib;
+  const KVX_CONST int64_t* sl = readonly(a.slots);
+
+  const char* sp[kCopyBatch];
+  int64_t tok[kCopyBatch], dof[kCopyBatch];
+  bool live[kCopyBatch];
+#pragma unroll
+  for (int j = 0; j < kCopyBatch; ++j) {
+    live[j] = s0 + j < a.total_slots;
+    tok[j] = t;
+    dof[j] = kv * a.kv_stride + piece * kWaveBytes;  // offset inside the token's slot
+    sp[j] = live[j] ? (kv ? a.value + t * a.value_stride : a.key + t * a.key_stride) + piece * kWaveBytes
+                    : a.key;  // idle slots re-read the first KiB of row 0
+    if (++piece == row_kib) {
+      piece = 0;
+      if (++kv == 2) { kv = 0; ++t; }
+    }
+  }
+  u32x4 v[kCopyBatch];
+#pragma unroll
+  for (int j = 0; j < kCopyBatch; ++j) v[j] = load16<NTL>(sp[j] + lane * kVec);
+
+  char* dp[kCopyBatch];
+  bool on[kCopyBatch];
+  bool bad = false;
+  int64_t cur = -1;
+  char* base = nullptr;
+  bool ok = false;
+#pragma unroll
+  for (int j = 0; j < kCopyBatch; ++j) {
+    if (live[j] && tok[j] != cur) {
+      cur = tok[j];
+      const int64_t s = sl[cur];
+      ok = false;
+      if (s >= 0) {
+        int64_t blk, off;
+        if (s <= 0x7fffffff) {
+          blk = (uint32_t)s / (uint32_t)a.block_size;
+          off = (uint32_t)s - (uint32_t)blk * (uint32_t)a.block_size;
+        } else {
+          blk = s / a.block_size;
+          off = s - blk * a.block_size;
+        }
+        if (blk < a.num_blocks) {
+          base = a.cache + blk * a.block_stride + off * a.token_stride;
+          ok = true;
+        } else {
+          bad = true;
+        }
+      }
+    }
+    on[j] = live[j] && ok;
+    dp[j] = base + dof[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kCopyBatch; ++j)
+    if (on[j]) store16<NTS>(dp[j] + lane * kVec, v[j]);
+  if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_SLOT_RANGE);
+}
+
 // --------------------------------------------------------------------------------------
 // a3 — transfer list: run-start flags -> workgroup prefix scan -> compaction
 // --------------------------------------------------------------------------------------
@@ -430,13 +528,6 @@ struct RunCopyArgs {
   int32_t xcd_remap;
 };
 
-constexpr int kCopyThreads = 256;
-constexpr int kCopyWavesPerWg = kCopyThreads / kWave;
-#ifndef KVX_COPY_BATCH
-#define KVX_COPY_BATCH 8
-#endif
-// 1 KiB wavefront loads a lane issues before its stores (8 -> 8 KiB in flight per wavefront)
-constexpr int kCopyBatch = KVX_COPY_BATCH;
 
 // Work split: wavefront w owns layer l = w / waves_per_layer and buffer positions
 // [c*B, min((c+1)*B, N)) of that layer (B = blocks_per_wave), so every wavefront moves the
@@ -925,6 +1016,34 @@ hipError_t launch_reshape_and_cache(const void* key, int64_t key_stride, const v
                                     int32_t block_size, int64_t block_stride,
                                     int64_t token_stride, int64_t kv_stride, int32_t* err,
                                     hipStream_t stream) {
+  const int64_t total_slots = num_tokens * 2 * (row_bytes / kWaveBytes);
+  if (row_bytes % kWaveBytes == 0 && tuning().one_batch &&
+      ceil_div(ceil_div(total_slots, kCopyBatch), 4) < ((int64_t)1 << 31)) {
+    WriteArgs a;
+    a.key = (const char*)key;
+    a.value = (const char*)value;
+    a.slots = slots;
+    a.cache = (char*)cache;
+    a.err = err;
+    a.key_stride = key_stride;
+    a.value_stride = value_stride;
+    a.num_tokens = num_tokens;
+    a.row_bytes = row_bytes;
+    a.num_blocks = num_blocks;
+    a.block_stride = block_stride;
+    a.token_stride = token_stride;
+    a.kv_stride = kv_stride;
+    a.total_slots = total_slots;
+    a.block_size = block_size;
+    const unsigned grid = (unsigned)ceil_div(ceil_div(total_slots, kCopyBatch), 4);
+    switch (tuning().write_nt & 3) {
+      case 0: write_slots_kernel<false, false><<<grid, 256, 0, stream>>>(a); break;
+      case 1: write_slots_kernel<true, false><<<grid, 256, 0, stream>>>(a); break;
+      case 2: write_slots_kernel<false, true><<<grid, 256, 0, stream>>>(a); break;
+      default: write_slots_kernel<true, true><<<grid, 256, 0, stream>>>(a); break;
+    }
+    return hipGetLastError();
+  }
   const int64_t wgs = ceil_div(num_tokens, 4);
   const unsigned grid = (unsigned)(wgs < (1 << 20) ? wgs : (1 << 20));
   reshape_and_cache_kernel<4><<<grid, 256, 0, stream>>>(

@@ -21,6 +21,7 @@ struct Tuning {
   CopyTuning pack, unpack, merge;
   int xcd_remap;  // 1: give each XCD a contiguous slice of the work (KVX_XCD_REMAP)
   int one_batch;  // 1: one-batch-per-wavefront kernels where blocks allow (KVX_ONE_BATCH)
+  int write_nt;   // cache policy of the new-token write, bits as nt_mode (KVX_NT_WRITE)
 };
 const Tuning& tuning();
 

@@ -288,3 +288,37 @@ def test_head_merge_small(S, H, D, rows_tok):
     for l in range(L):
         assert np.array_equal(host_bytes(dst[l]).reshape(exp[l].shape), exp[l]), l
     assert int(err.item()) == eerr == 0
+
+
+@pytest.mark.parametrize("H,D", [(4, 128), (8, 128), (16, 128), (32, 128), (2, 256)])
+@pytest.mark.parametrize("layout", ["blocks_tokens_kv", "blocks_kv_tokens", "kv_blocks_tokens"])
+def test_reshape_and_cache_whole_kib_rows(H, D, layout):
+    """Rows of 1, 2, 4 and 8 KiB take the one-batch write kernel (8 KiB rows spread one token
+    over two wavefronts); padding tokens and a slot past the cache included."""
+    d = W.decode_write(seed=H * 1000 + D, num_reqs=7, max_len=150, num_blocks=96, num_kv_heads=H, head_dim=D)
+    slots, _ = O.slot_mapping(d.block_table, d.req_idx, d.positions, 16)
+    slots = slots.copy()
+    slots[5::11] = -1
+    slots[2] = 96 * 16 + 3
+    _reshape_check(d, layout, slots)
+
+
+def test_reshape_and_cache_strided_rows():
+    """K and V as views into one fused [T][3][H][D] tensor (row stride 3 rows)."""
+    K = kvx()
+    d = W.decode_write(seed=77, num_reqs=5, max_len=90, num_blocks=64, num_kv_heads=8, head_dim=128)
+    T = len(d.req_idx)
+    s = d.spec
+    slots, _ = O.slot_mapping(d.block_table, d.req_idx, d.positions, 16)
+    fused = np.zeros((T, 3, 8, 128), np.uint16)
+    fused[:, 1] = d.key
+    fused[:, 2] = d.value
+    fused_d = to_dev(fused)
+    cache_h = np.full(s.shape5, W.SENTINEL16, np.uint16)
+    cache = to_dev(cache_h)
+    nb, bs, bst, tst, kst = K.cache_strides(cache)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    K.kvx_reshape_and_cache(fused_d[:, 1], fused_d[:, 2], to_dev(slots), cache, nb, bs, bst, tst, kst, err)
+    torch.cuda.synchronize()
+    exp, e = O.reshape_and_cache(cache_h, d.key, d.value, slots, nb, bs, bst, tst, kst)
+    assert np.array_equal(host_bytes(cache), exp) and int(err.item()) == e == 0
