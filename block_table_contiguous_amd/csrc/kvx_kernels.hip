@@ -32,9 +32,16 @@ static int64_t env_i64(const char* name, int64_t dflt) {
 
 const Tuning& tuning() {
   static const Tuning t = {
-      {env_i64("KVX_WAVE_BYTES_PACK", 8 * 1024), (int)env_i64("KVX_NT_PACK", 3)},
-      {env_i64("KVX_WAVE_BYTES_UNPACK", 8 * 1024), (int)env_i64("KVX_NT_UNPACK", 3)},
-      {env_i64("KVX_WAVE_BYTES_MERGE", 64 * 1024), (int)env_i64("KVX_NT_MERGE", 3)},
+      {env_i64("KVX_WAVE_BYTES_PACK", 8 * 1024), (int)env_i64("KVX_NT_PACK", 3),
+       (int)env_i64("KVX_BATCH_PACK", 4)},
+      {env_i64("KVX_WAVE_BYTES_UNPACK", 8 * 1024), (int)env_i64("KVX_NT_UNPACK", 3),
+       (int)env_i64("KVX_BATCH_UNPACK", 8)},
+      {env_i64("KVX_WAVE_BYTES_MERGE", 64 * 1024), (int)env_i64("KVX_NT_MERGE", 3),
+       (int)env_i64("KVX_BATCH_MERGE", 8)},
+      {env_i64("KVX_WAVE_BYTES_SPLIT", 64 * 1024), (int)env_i64("KVX_NT_SPLIT", 3),
+       (int)env_i64("KVX_BATCH_SPLIT", 4)},
+      {0, (int)env_i64("KVX_NT_KVF_PACK", 3), (int)env_i64("KVX_BATCH_KVF_PACK", 8)},
+      {0, (int)env_i64("KVX_NT_KVF_UNPACK", 3), (int)env_i64("KVX_BATCH_KVF_UNPACK", 8)},
       (int)env_i64("KVX_XCD_REMAP", 1),
       (int)env_i64("KVX_ONE_BATCH", 1),
       (int)env_i64("KVX_NT_WRITE", 1),
@@ -76,7 +83,10 @@ constexpr int kVec = 16;                 // bytes per lane access
 constexpr int kWaveBytes = kWave * kVec; // bytes per wavefront instruction
 constexpr int kNumXcd = 8;               // MI355X: 8 XCDs, workgroups dealt round-robin
 
-constexpr int kCopyThreads = 256;
+#ifndef KVX_COPY_THREADS
+#define KVX_COPY_THREADS 256
+#endif
+constexpr int kCopyThreads = KVX_COPY_THREADS;
 constexpr int kCopyWavesPerWg = kCopyThreads / kWave;
 #ifndef KVX_COPY_BATCH
 #define KVX_COPY_BATCH 8
@@ -689,17 +699,17 @@ __global__ __launch_bounds__(kCopyThreads) void shard_runs_kernel(ShardArgs a) {
 // one-batch fast paths (block rows in whole KiB)
 // --------------------------------------------------------------------------------------
 
-// Bytes one wavefront moves in the fast paths: one batch of kCopyBatch 1 KiB instructions.
-constexpr int64_t kUnitBytes = (int64_t)kCopyBatch * kWaveBytes;
+// In the fast paths a wavefront moves one batch of K 1 KiB instructions (K KiB); K is chosen
+// per kernel at launch (4 or 8).
 
 // Pack / single-source unpack when block_bytes is a multiple of 1 KiB (a 16-token block of
-// K,V x heads x head_dim x 2 B always is). Wavefront w owns kUnitBytes of one layer's buffer
-// slice; each of its kCopyBatch instruction slots lies inside one block. The slot addresses
+// K,V x heads x head_dim x 2 B always is). Wavefront w owns K KiB of one layer's buffer
+// slice; each of its K instruction slots lies inside one block. The slot addresses
 // are worked out on the scalar unit (walking the runs from the one holding the first block),
 // then the wavefront issues all its loads, then all its stores, and exits. On this
 // architecture stores count in vmcnt, so a wavefront with a second batch would wait for its
 // first batch's store acknowledgements; one batch per wavefront never does.
-template <bool TO_BUFFER, bool NTL, bool NTS>
+template <bool TO_BUFFER, bool NTL, bool NTS, int K>
 __global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(RunCopyArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t wg = blockIdx.x;
@@ -718,7 +728,7 @@ __global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(RunCopyArgs a)
   char* cache = const_cast<char*>(*readonly(a.layer_bases + l));
   char* buf = a.buffer + l * layer_bytes;
 
-  const int64_t o0 = u * kUnitBytes;
+  const int64_t o0 = u * ((int64_t)K * kWaveBytes);
   int64_t q = o0 / BB;       // buffer position of the first slot
   int64_t off = o0 - q * BB; // byte offset inside that block (a multiple of 1 KiB)
   int64_t k = uniform(find_run(a.xfers, count, q, lane));
@@ -727,12 +737,12 @@ __global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(RunCopyArgs a)
   // Slots with nothing to move load from `idle` (1 KiB of this wavefront's own buffer range,
   // always inside the allocation) so every load is unconditional; only stores are skipped.
   const char* idle = buf + o0;
-  const char* sp[kCopyBatch];
-  char* dp[kCopyBatch];
-  bool on[kCopyBatch];
+  const char* sp[K];
+  char* dp[K];
+  bool on[K];
   bool bad = false;
 #pragma unroll
-  for (int j = 0; j < kCopyBatch; ++j) {
+  for (int j = 0; j < K; ++j) {
     const int64_t o = o0 + (int64_t)j * kWaveBytes;
     on[j] = false;
     sp[j] = idle;
@@ -755,21 +765,21 @@ __global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(RunCopyArgs a)
     off += kWaveBytes;
     if (off == BB) { off = 0; ++q; }
   }
-  u32x4 v[kCopyBatch];
+  u32x4 v[K];
 #pragma unroll
-  for (int j = 0; j < kCopyBatch; ++j) v[j] = load16<NTL>(sp[j] + lane * kVec);
+  for (int j = 0; j < K; ++j) v[j] = load16<NTL>(sp[j] + lane * kVec);
 #pragma unroll
-  for (int j = 0; j < kCopyBatch; ++j)
+  for (int j = 0; j < K; ++j)
     if (on[j]) store16<NTS>(dp[j] + lane * kVec, v[j]);
   if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_BLOCK_RANGE);
 }
 
-// Head shards when a row piece is a multiple of 1 KiB. Wavefront w owns kUnitBytes of one
+// Head shards when a row piece is a multiple of 1 KiB. Wavefront w owns K KiB of one
 // layer's cache-side bytes taken in buffer order (position q, then row, then shard, then
 // byte); slot j is the 1 KiB at offset w_in of the cache block for position q, which is
 // bytes [xo, xo + 1 KiB) of row `row` of shard d. Counters step (xo, d, row, q) without
 // divisions. TO_BUFFER = split (cache -> shards), otherwise merge (shards -> cache).
-template <bool TO_BUFFER, bool NTL, bool NTS>
+template <bool TO_BUFFER, bool NTL, bool NTS, int K>
 __global__ __launch_bounds__(kCopyThreads) void shard_slots_kernel(ShardArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t wg = blockIdx.x;
@@ -791,7 +801,7 @@ __global__ __launch_bounds__(kCopyThreads) void shard_slots_kernel(ShardArgs a) 
   if (count <= 0) return;
   char* cache = const_cast<char*>(*readonly(a.layer_bases + l));
 
-  const int64_t o0 = u * kUnitBytes;
+  const int64_t o0 = u * ((int64_t)K * kWaveBytes);
   int64_t q = o0 / BB;
   int64_t w_in = o0 - q * BB;
   int64_t row = w_in / row_full;
@@ -803,12 +813,12 @@ __global__ __launch_bounds__(kCopyThreads) void shard_slots_kernel(ShardArgs a) 
   Run x = load_run(xf, k);
   // Idle slots load the first KiB of shard 0's layer slice (always in bounds).
   const char* idle = a.shard[0] + l * N * BBs;
-  const char* sp[kCopyBatch];
-  char* dp[kCopyBatch];
-  bool on[kCopyBatch];
+  const char* sp[K];
+  char* dp[K];
+  bool on[K];
   bool bad = false;
 #pragma unroll
-  for (int j = 0; j < kCopyBatch; ++j) {
+  for (int j = 0; j < K; ++j) {
     const int64_t o = o0 + (int64_t)j * kWaveBytes;
     on[j] = false;
     sp[j] = idle;
@@ -836,11 +846,11 @@ __global__ __launch_bounds__(kCopyThreads) void shard_slots_kernel(ShardArgs a) 
     }
     if (w_in == BB) { w_in = 0; row = 0; d = 0; xo = 0; ++q; }
   }
-  u32x4 v[kCopyBatch];
+  u32x4 v[K];
 #pragma unroll
-  for (int j = 0; j < kCopyBatch; ++j) v[j] = load16<NTL>(sp[j] + lane * kVec);
+  for (int j = 0; j < K; ++j) v[j] = load16<NTL>(sp[j] + lane * kVec);
 #pragma unroll
-  for (int j = 0; j < kCopyBatch; ++j)
+  for (int j = 0; j < K; ++j)
     if (on[j]) store16<NTS>(dp[j] + lane * kVec, v[j]);
   if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_BLOCK_RANGE);
 }
@@ -888,11 +898,11 @@ __device__ __forceinline__ int64_t find_segment_request(const int64_t* __restric
 
 // The buffer slice of layer l is, per request r, its K segments in table order, then its V
 // segments (what a gather along the block axis of a (2, blocks, ...) tensor returns).
-// Wavefront w owns kUnitBytes of that slice: slot j is 1 KiB of segment g, which belongs to
+// Wavefront w owns K KiB of that slice: slot j is 1 KiB of segment g, which belongs to
 // request r, plane `plane` and table index jj, i.e. position p = cum_r + jj. Runs never
 // span requests, so p walks the runs of request r once per plane; the wavefront keeps the
 // index of the request's first run to restart the walk for the V plane.
-template <bool TO_BUFFER, bool NTL, bool NTS>
+template <bool TO_BUFFER, bool NTL, bool NTS, int K>
 __global__ __launch_bounds__(kCopyThreads) void kv_first_kernel(KvFirstArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t wg = blockIdx.x;
@@ -913,7 +923,7 @@ __global__ __launch_bounds__(kCopyThreads) void kv_first_kernel(KvFirstArgs a) {
   char* cache = const_cast<char*>(*readonly(a.layer_bases + l));
   char* buf = a.buffer + l * layer_bytes;
 
-  const int64_t o0 = u * kUnitBytes;
+  const int64_t o0 = u * ((int64_t)K * kWaveBytes);
   int64_t g = o0 / SEG;
   int64_t in_seg = o0 - g * SEG;
   int64_t r = uniform(find_segment_request(a.req_offsets, R, g, lane));
@@ -929,12 +939,12 @@ __global__ __launch_bounds__(kCopyThreads) void kv_first_kernel(KvFirstArgs a) {
   if (k < 0) k = 0;
   Run x = load_run(xf, k);
   const char* idle = buf + o0;
-  const char* sp[kCopyBatch];
-  char* dp[kCopyBatch];
-  bool on[kCopyBatch];
+  const char* sp[K];
+  char* dp[K];
+  bool on[K];
   bool bad = false;
 #pragma unroll
-  for (int j = 0; j < kCopyBatch; ++j) {
+  for (int j = 0; j < K; ++j) {
     const int64_t o = o0 + (int64_t)j * kWaveBytes;
     on[j] = false;
     sp[j] = idle;
@@ -983,11 +993,11 @@ __global__ __launch_bounds__(kCopyThreads) void kv_first_kernel(KvFirstArgs a) {
       }
     }
   }
-  u32x4 v[kCopyBatch];
+  u32x4 v[K];
 #pragma unroll
-  for (int j = 0; j < kCopyBatch; ++j) v[j] = load16<NTL>(sp[j] + lane * kVec);
+  for (int j = 0; j < K; ++j) v[j] = load16<NTL>(sp[j] + lane * kVec);
 #pragma unroll
-  for (int j = 0; j < kCopyBatch; ++j)
+  for (int j = 0; j < K; ++j)
     if (on[j]) store16<NTS>(dp[j] + lane * kVec, v[j]);
   if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_BLOCK_RANGE);
 }
@@ -1072,27 +1082,26 @@ static int64_t blocks_per_wave_for(int64_t wave_bytes, int64_t block_bytes, int6
   return bpw > min_bpw ? bpw : min_bpw;
 }
 
-template <bool TO_BUFFER, bool NTL, bool NTS>
-static void launch_copy_policy(const RunCopyArgs& a, bool slots, unsigned grid, hipStream_t stream) {
-  if (slots) copy_slots_kernel<TO_BUFFER, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
-  else copy_runs_kernel<TO_BUFFER, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
-}
-
-template <bool TO_BUFFER>
-static void launch_copy_variant(const RunCopyArgs& a, int nt_mode, bool slots, unsigned grid,
-                                hipStream_t stream) {
-  switch (nt_mode & 3) {
-    case 0: launch_copy_policy<TO_BUFFER, false, false>(a, slots, grid, stream); break;
-    case 1: launch_copy_policy<TO_BUFFER, true, false>(a, slots, grid, stream); break;
-    case 2: launch_copy_policy<TO_BUFFER, false, true>(a, slots, grid, stream); break;
-    default: launch_copy_policy<TO_BUFFER, true, true>(a, slots, grid, stream); break;
+// Runtime (cache policy, batch) -> template instance. LAUNCH(NTL, NTS, K) launches one.
+#define KVX_POLICY_SWITCH(NT, K, LAUNCH)          \
+  switch (((NT) & 3) * 2 + ((K) <= 4 ? 0 : 1)) { \
+    case 0: LAUNCH(false, false, 4) break;        \
+    case 1: LAUNCH(false, false, 8) break;        \
+    case 2: LAUNCH(true, false, 4) break;         \
+    case 3: LAUNCH(true, false, 8) break;         \
+    case 4: LAUNCH(false, true, 4) break;         \
+    case 5: LAUNCH(false, true, 8) break;         \
+    case 6: LAUNCH(true, true, 4) break;          \
+    default: LAUNCH(true, true, 8) break;         \
   }
-}
 
-// The one-batch fast path needs whole-KiB blocks and a grid that fits 32-bit workgroup ids.
-static bool use_slots(int64_t unit_bytes_ok, int64_t num_layers, int64_t layer_bytes) {
-  if (!unit_bytes_ok || !tuning().one_batch) return false;
-  const int64_t waves = num_layers * ceil_div(layer_bytes, kUnitBytes);
+// Batch of the one-batch kernels: 4 or 8 KiB per wavefront.
+static int batch_of(const CopyTuning& ct) { return ct.batch <= 4 ? 4 : 8; }
+
+// The one-batch fast path needs whole-KiB rows and a grid that fits 32-bit workgroup ids.
+static bool use_slots(bool whole_kib, int64_t num_layers, int64_t layer_bytes, int64_t unit) {
+  if (!whole_kib || !tuning().one_batch) return false;
+  const int64_t waves = num_layers * ceil_div(layer_bytes, unit);
   return ceil_div(waves, kCopyWavesPerWg) < ((int64_t)1 << 31);
 }
 
@@ -1110,10 +1119,12 @@ hipError_t launch_copy_runs(bool to_buffer, void* const* layer_bases, int32_t nu
   a.num_cache_blocks = num_cache_blocks;
   a.total_blocks = total_blocks;
   const CopyTuning& ct = to_buffer ? tuning().pack : tuning().unpack;
-  const bool slots = use_slots(block_bytes % kWaveBytes == 0, num_layers, total_blocks * block_bytes);
-  if (slots) {  // one kUnitBytes batch per wavefront
+  const int K = batch_of(ct);
+  const int64_t unit = (int64_t)K * kWaveBytes;
+  const bool slots = use_slots(block_bytes % kWaveBytes == 0, num_layers, total_blocks * block_bytes, unit);
+  if (slots) {  // one K KiB batch per wavefront
     a.blocks_per_wave = 0;
-    a.waves_per_layer = ceil_div(total_blocks * block_bytes, kUnitBytes);
+    a.waves_per_layer = ceil_div(total_blocks * block_bytes, unit);
   } else {      // general path: whole blocks, about wave_bytes per wavefront
     a.blocks_per_wave = blocks_per_wave_for(ct.wave_bytes, block_bytes, num_layers, total_blocks);
     a.waves_per_layer = ceil_div(total_blocks, a.blocks_per_wave);
@@ -1123,8 +1134,16 @@ hipError_t launch_copy_runs(bool to_buffer, void* const* layer_bases, int32_t nu
   a.num_layers = num_layers;
   a.xcd_remap = tuning().xcd_remap;
   const unsigned grid = (unsigned)a.num_wgs;
-  if (to_buffer) launch_copy_variant<true>(a, ct.nt_mode, slots, grid, stream);
-  else launch_copy_variant<false>(a, ct.nt_mode, slots, grid, stream);
+#define KVX_COPY_T(NTL, NTS, KB)                                                           \
+  if (slots) copy_slots_kernel<true, NTL, NTS, KB><<<grid, kCopyThreads, 0, stream>>>(a); \
+  else copy_runs_kernel<true, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
+#define KVX_COPY_F(NTL, NTS, KB)                                                            \
+  if (slots) copy_slots_kernel<false, NTL, NTS, KB><<<grid, kCopyThreads, 0, stream>>>(a); \
+  else copy_runs_kernel<false, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
+  if (to_buffer) { KVX_POLICY_SWITCH(ct.nt_mode, K, KVX_COPY_T) }
+  else { KVX_POLICY_SWITCH(ct.nt_mode, K, KVX_COPY_F) }
+#undef KVX_COPY_T
+#undef KVX_COPY_F
   return hipGetLastError();
 }
 
@@ -1143,11 +1162,13 @@ hipError_t launch_shards(bool to_buffer, void* const* shards, int32_t num_shards
   a.num_cache_blocks = num_cache_blocks;
   a.total_blocks = total_blocks;
   a.row_piece = block_bytes / ((int64_t)rows_per_block * num_shards);
-  const CopyTuning& ct = to_buffer ? tuning().pack : tuning().merge;
-  const bool slots = use_slots(a.row_piece % kWaveBytes == 0, num_layers, total_blocks * block_bytes);
+  const CopyTuning& ct = to_buffer ? tuning().split : tuning().merge;
+  const int K = batch_of(ct);
+  const int64_t unit = (int64_t)K * kWaveBytes;
+  const bool slots = use_slots(a.row_piece % kWaveBytes == 0, num_layers, total_blocks * block_bytes, unit);
   if (slots) {
     a.blocks_per_wave = 0;
-    a.waves_per_layer = ceil_div(total_blocks * block_bytes, kUnitBytes);
+    a.waves_per_layer = ceil_div(total_blocks * block_bytes, unit);
   } else {
     a.blocks_per_wave = blocks_per_wave_for(ct.wave_bytes, block_bytes, num_layers, total_blocks);
     a.waves_per_layer = ceil_div(total_blocks, a.blocks_per_wave);
@@ -1159,20 +1180,16 @@ hipError_t launch_shards(bool to_buffer, void* const* shards, int32_t num_shards
   a.num_layers = num_layers;
   a.xcd_remap = tuning().xcd_remap;
   const unsigned grid = (unsigned)a.num_wgs;
-#define KVX_SHARD_LAUNCH(TB, NTL, NTS)                                                   \
-  if (slots) shard_slots_kernel<TB, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);    \
-  else shard_runs_kernel<TB, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
-#define KVX_SHARD_POLICY(TB)                            \
-  switch (ct.nt_mode & 3) {                             \
-    case 0: KVX_SHARD_LAUNCH(TB, false, false) break;   \
-    case 1: KVX_SHARD_LAUNCH(TB, true, false) break;    \
-    case 2: KVX_SHARD_LAUNCH(TB, false, true) break;    \
-    default: KVX_SHARD_LAUNCH(TB, true, true) break;    \
-  }
-  if (to_buffer) { KVX_SHARD_POLICY(true) }
-  else { KVX_SHARD_POLICY(false) }
-#undef KVX_SHARD_POLICY
-#undef KVX_SHARD_LAUNCH
+#define KVX_SHARD_T(NTL, NTS, KB)                                                           \
+  if (slots) shard_slots_kernel<true, NTL, NTS, KB><<<grid, kCopyThreads, 0, stream>>>(a); \
+  else shard_runs_kernel<true, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
+#define KVX_SHARD_F(NTL, NTS, KB)                                                            \
+  if (slots) shard_slots_kernel<false, NTL, NTS, KB><<<grid, kCopyThreads, 0, stream>>>(a); \
+  else shard_runs_kernel<false, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
+  if (to_buffer) { KVX_POLICY_SWITCH(ct.nt_mode, K, KVX_SHARD_T) }
+  else { KVX_POLICY_SWITCH(ct.nt_mode, K, KVX_SHARD_F) }
+#undef KVX_SHARD_T
+#undef KVX_SHARD_F
   return hipGetLastError();
 }
 
@@ -1192,25 +1209,24 @@ hipError_t launch_kv_first(bool to_buffer, void* const* layer_bases, int32_t num
   a.plane_stride = plane_stride;
   a.num_cache_blocks = num_cache_blocks;
   a.total_blocks = total_blocks;
-  a.waves_per_layer = ceil_div(2 * total_blocks * segment_bytes, kUnitBytes);
+  const CopyTuning& ct = to_buffer ? tuning().kvf_pack : tuning().kvf_unpack;
+  const int K = batch_of(ct);
+  a.waves_per_layer = ceil_div(2 * total_blocks * segment_bytes, (int64_t)K * kWaveBytes);
   a.total_waves = a.waves_per_layer * num_layers;
   a.num_wgs = ceil_div(a.total_waves, kCopyWavesPerWg);
   a.num_reqs = num_reqs;
   a.num_layers = num_layers;
   a.xcd_remap = tuning().xcd_remap;
   const unsigned grid = (unsigned)a.num_wgs;
-  const int nt = (to_buffer ? tuning().pack : tuning().unpack).nt_mode & 3;
-#define KVX_KVF_LAUNCH(TB)                                                                       \
-  switch (nt) {                                                                                  \
-    case 0: kv_first_kernel<TB, false, false><<<grid, kCopyThreads, 0, stream>>>(a); break;      \
-    case 1: kv_first_kernel<TB, true, false><<<grid, kCopyThreads, 0, stream>>>(a); break;       \
-    case 2: kv_first_kernel<TB, false, true><<<grid, kCopyThreads, 0, stream>>>(a); break;       \
-    default: kv_first_kernel<TB, true, true><<<grid, kCopyThreads, 0, stream>>>(a); break;       \
-  }
-  if (to_buffer) { KVX_KVF_LAUNCH(true) }
-  else { KVX_KVF_LAUNCH(false) }
-#undef KVX_KVF_LAUNCH
+#define KVX_KVF_T(NTL, NTS, KB) kv_first_kernel<true, NTL, NTS, KB><<<grid, kCopyThreads, 0, stream>>>(a);
+#define KVX_KVF_F(NTL, NTS, KB) kv_first_kernel<false, NTL, NTS, KB><<<grid, kCopyThreads, 0, stream>>>(a);
+  if (to_buffer) { KVX_POLICY_SWITCH(ct.nt_mode, K, KVX_KVF_T) }
+  else { KVX_POLICY_SWITCH(ct.nt_mode, K, KVX_KVF_F) }
+#undef KVX_KVF_T
+#undef KVX_KVF_F
   return hipGetLastError();
 }
+
+#undef KVX_POLICY_SWITCH
 
 }  // namespace kvx

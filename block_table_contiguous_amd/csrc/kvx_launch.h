@@ -11,14 +11,15 @@ namespace kvx {
 
 // Launch-shape knobs. Defaults are compiled in; each can be overridden once per process
 // through the environment (read on first use) so sweeps need no rebuild.
-// Per copy kernel: bytes of buffer one wavefront owns, and the cache policy
-// (bit 0: non-temporal loads, bit 1: non-temporal stores).
+// Per copy kernel: bytes of buffer one wavefront owns, the cache policy (bit 0:
+// non-temporal loads, bit 1: non-temporal stores) and the batch of the one-batch kernels.
 struct CopyTuning {
-  int64_t wave_bytes;  // KVX_WAVE_BYTES_{PACK,UNPACK,MERGE}
-  int nt_mode;         // KVX_NT_{PACK,UNPACK,MERGE}
+  int64_t wave_bytes;  // general path (KVX_WAVE_BYTES_{PACK,UNPACK,MERGE,SPLIT})
+  int nt_mode;         // KVX_NT_{PACK,UNPACK,MERGE,SPLIT}
+  int batch;           // one-batch path: KiB per wavefront, 4 or 8 (KVX_BATCH_{...})
 };
 struct Tuning {
-  CopyTuning pack, unpack, merge;
+  CopyTuning pack, unpack, merge, split, kvf_pack, kvf_unpack;
   int xcd_remap;  // 1: give each XCD a contiguous slice of the work (KVX_XCD_REMAP)
   int one_batch;  // 1: one-batch-per-wavefront kernels where blocks allow (KVX_ONE_BATCH)
   int write_nt;   // cache policy of the new-token write, bits as nt_mode (KVX_NT_WRITE)
