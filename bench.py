@@ -251,6 +251,7 @@ def main():
     for n in ("pack", "unpack"):
         out_ops[n]["GB/s"] = round(copy_bytes / (kern[n] * 1e-3) / 1e9, 1)
         out_ops[n]["frac_of_peak"] = round(copy_bytes / (kern[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        out_ops[n]["traffic"] = traffic_from_counters(f"{n}_{case.name}", copy_bytes)
     runs_pack, runs_unpack = int(cp.item()), int(cu.item())
     out_ops["build_pack"]["runs"] = runs_pack
     out_ops["build_unpack"]["runs"] = runs_unpack
@@ -274,7 +275,8 @@ def main():
             med, mn = time_op(torch, fn, args.op_reps, flush)
             out_ops[n] = {"workload": f"{case.name}, kv-first view: 48 x (2, {nb}, {seg} B)",
                           "median_ms": round(med, 5), "GB/s": round(copy_bytes / (med * 1e-3) / 1e9, 1),
-                          "frac_of_peak": round(copy_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                          "frac_of_peak": round(copy_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                          "traffic": traffic_from_counters(f"{n}_{case.name}", copy_bytes)}
         torch.cuda.synchronize()
         assert int(err.item()) == 0, "device error flag raised"
         out_ops.update(other_workloads(torch, np, W, K, dev, flush, args.op_reps))
@@ -341,7 +343,8 @@ def other_workloads(torch, np, W, K, dev, flush, reps):
     out["split_pack_asym_tp"] = {
         "workload": "32 layers of [8192][16][K,V][8][128] bf16, 16 requests x 256 blocks -> 2 shards x 4 heads",
         "bytes": nbytes, "median_ms": round(med, 4), "min_ms": round(mn, 4),
-        "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "traffic": traffic_from_counters("split_asym_tp", nbytes)}
     del srcs, dst
     # decode write: 32 requests of 1..2048 tokens into a [4096][16][K,V][8][128] bf16 cache
     d = W.decode_write()
@@ -360,7 +363,8 @@ def other_workloads(torch, np, W, K, dev, flush, reps):
     wbytes = T * (4 * d.spec.row_bytes + 8)
     out["reshape_and_cache_decode"] = {
         "tokens": T, "bytes": wbytes, "median_ms": round(med, 5),
-        "GB/s": round(wbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(wbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        "GB/s": round(wbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(wbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "traffic": traffic_from_counters("write_decode", wbytes)}
     return out
 
 
