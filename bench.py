@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_table_contiguous_amd", "csrc", f)
-                  for f in ("kvx_kernels.hip", "kvx_launch.h", "kvx_api.hip")]
+                  for f in ("kvx_kernels.hip", "kvx_launch.h")]
 
 
 def log(msg):
@@ -279,6 +279,8 @@ def main():
                           "traffic": traffic_from_counters(f"{n}_{case.name}", copy_bytes)}
         torch.cuda.synchronize()
         assert int(err.item()) == 0, "device error flag raised"
+        out_ops["layer_pipeline"] = layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err,
+                                                   max(3, args.op_reps // 2))
         out_ops.update(other_workloads(torch, np, W, K, dev, flush, args.op_reps))
 
     cpu = None
@@ -313,6 +315,80 @@ def main():
         "kernel_source_sha256_16": kernel_source_hash(),
     }
     print(json.dumps(result), flush=True)
+
+
+def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, reps):
+    """The sender's side of a layer-pipelined transfer. One bf16 [8192 x 4096] x [4096 x 4096]
+    product per layer on the forward stream stands in for that layer's forward pass (it is not
+    part of the path). Schedules, each timed from a start event to the end of all streams, with
+    the tail (end of the last product to the end of the packing) beside it:
+      forward_only  the 48 products;
+      serial        the 48 products, then one pack of all layers on the forward stream;
+      pipelined     per layer: the product, then an event on the forward stream; on a copy
+                    stream, a wait for that event, the pack of that layer into its slice of the
+                    send buffer and a signal add — the count a transport (or a receiver's
+                    signal wait) follows layer by layer. The forward stream never waits for a
+                    copy.
+    The receiver's unpack is left out here: it runs on the other GPU of a real transfer, not
+    beside the sender's forward pass."""
+    m, k = 8192, 4096
+    a = torch.full((m, k), 0.5, dtype=torch.bfloat16, device=dev)
+    b = torch.full((k, k), 0.25, dtype=torch.bfloat16, device=dev)
+    c = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    fwd, cpy = torch.cuda.Stream(), torch.cuda.Stream()
+    counter = torch.zeros(1, dtype=torch.int64, device=dev)
+    bufv = buf[: L * N * BB].view(L, N, BB)
+    evs = [torch.cuda.Event() for _ in range(L)]
+    pack_l = [src_bases[l:l + 1] for l in range(L)]
+
+    def forward_only(f_ev):
+        with torch.cuda.stream(fwd):
+            for _ in range(L):
+                torch.mm(a, b, out=c)
+            f_ev.record(fwd)
+
+    def serial(f_ev):
+        with torch.cuda.stream(fwd):
+            for _ in range(L):
+                torch.mm(a, b, out=c)
+            f_ev.record(fwd)
+            K.kvx_pack(src_bases, BB, nb, xp, cp, N, buf, err, stream=fwd)
+
+    def pipelined(f_ev):
+        for l in range(L):
+            with torch.cuda.stream(fwd):
+                torch.mm(a, b, out=c)
+                evs[l].record(fwd)
+            cpy.wait_event(evs[l])
+            K.kvx_pack(pack_l[l], BB, nb, xp, cp, N, bufv[l], err, stream=cpy)
+            K.kvx_signal_add(counter, 1, stream=cpy)
+        f_ev.record(fwd)
+
+    def run(fn):
+        torch.cuda.synchronize()
+        s_ev, f_ev, e_ev = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        s_ev.record(fwd)
+        cpy.wait_stream(fwd)
+        fn(f_ev)
+        fwd.wait_stream(cpy)
+        e_ev.record(fwd)
+        torch.cuda.synchronize()
+        return s_ev.elapsed_time(e_ev), f_ev.elapsed_time(e_ev)
+
+    out = {"workload": f"{L} layers; forward stream: one bf16 [{m}x{k}]x[{k}x{k}] product per layer "
+                       "(forward stand-in); copy stream: that layer's pack, then a signal add"}
+    for name, fn in (("forward_only", forward_only), ("serial", serial), ("pipelined", pipelined)):
+        run(fn)  # warm
+        ts = sorted(run(fn) for _ in range(reps))
+        total, tail = ts[len(ts) // 2]
+        out[f"{name}_ms"] = round(total, 4)
+        if name != "forward_only":
+            out[f"{name}_tail_ms"] = round(tail, 4)
+        log(f"layer pipeline {name}: {total:.4f} ms, tail after the forward {tail:.4f} ms")
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, "device error flag raised"
+    assert int(counter.item()) == L * (reps + 1), "signal count"
+    return out
 
 
 def other_workloads(torch, np, W, K, dev, flush, reps):

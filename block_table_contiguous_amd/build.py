@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvx.so")
-SOURCES = ["kvx_api.hip", "kvx_kernels.hip"]
+SOURCES = ["kvx_api.hip", "kvx_kernels.hip", "kvx_signal.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for all device code (the kernels do no float

@@ -31,7 +31,7 @@ const char* kvx_status_string(kvx_status status) {
   return "kvx: unknown status";
 }
 
-int32_t kvx_abi_version(void) { return 2; }
+int32_t kvx_abi_version(void) { return 3; }
 
 kvx_status kvx_slot_mapping(const int32_t* block_table, int64_t num_reqs,
                             int64_t max_blocks_per_req, int64_t bt_row_stride,

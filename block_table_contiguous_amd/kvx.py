@@ -31,6 +31,7 @@ DEVERR_BLOCK_RANGE = 1
 DEVERR_TABLE_RANGE = 2
 DEVERR_SLOT_RANGE = 4
 DEVERR_OFFSETS = 8
+DEVERR_TIMEOUT = 16
 
 MODE_PACK, MODE_UNPACK, MODE_DIRECT = 0, 1, 2
 MAX_SOURCES = 8
@@ -53,6 +54,8 @@ SIGNATURES = {
     "kvx_pack_split": (ctypes.c_int, [_P, _I32, _I64, _I64, _I32, _P, _P, _I64, _P, _I32, _P, _P]),
     "kvx_pack_kv_first": (ctypes.c_int, [_P, _I32, _I64, _I64, _I64, _P, _I32, _P, _P, _I64, _P, _P, _P]),
     "kvx_unpack_kv_first": (ctypes.c_int, [_P, _P, _I32, _I64, _I64, _I64, _P, _I32, _P, _P, _I64, _P, _P]),
+    "kvx_signal_add": (ctypes.c_int, [_P, ctypes.c_uint64, _P]),
+    "kvx_signal_wait": (ctypes.c_int, [_P, ctypes.c_uint64, _I64, _P, _P]),
 }
 
 
@@ -340,3 +343,24 @@ def kvx_unpack_kv_first(send_buf, layer_bases, segment_bytes: int, plane_stride_
                                    req_offsets.numel() - 1, _ptr(xfers), _ptr(xfer_count), int(total_blocks),
                                    _ptr(err_flag), _stream(stream))
     _check("kvx_unpack_kv_first", st)
+
+
+def kvx_signal_add(counter, delta: int = 1, stream=None):
+    """Once the work enqueued on `stream` so far has finished, add `delta` to the uint64
+    counter (an int64 device tensor of one element, read as unsigned)."""
+    _want(counter, _torch_int64(), "counter")
+    _check("kvx_signal_add", _F["kvx_signal_add"](_ptr(counter), int(delta), _stream(stream)))
+
+
+def kvx_signal_wait(counter, value: int, timeout_us: int = 10_000_000, err=None, stream=None):
+    """Hold the work enqueued on `stream` after this call until counter >= value (polled on
+    the GPU); after timeout_us the wait ends and sets DEVERR_TIMEOUT in `err`."""
+    _want(counter, _torch_int64(), "counter")
+    _check("kvx_signal_wait", _F["kvx_signal_wait"](_ptr(counter), int(value), int(timeout_us),
+                                                    _ptr(err), _stream(stream)))
+
+
+def _torch_int64():
+    import torch
+
+    return torch.int64

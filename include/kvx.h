@@ -57,6 +57,7 @@ typedef enum kvx_status {
 #define KVX_DEVERR_TABLE_RANGE 2 /* slot mapping: request index or position off the table */
 #define KVX_DEVERR_SLOT_RANGE 4  /* new-token write: slot in a block >= num_blocks         */
 #define KVX_DEVERR_OFFSETS 8     /* run building: req_offsets is not a CSR over the blocks */
+#define KVX_DEVERR_TIMEOUT 16    /* signal wait: the counter did not reach its value in time */
 
 /* Which side(s) of a transfer a run must be +1-consecutive on. */
 #define KVX_MODE_PACK 0   /* cache -> buffer: runs consecutive in the source ids        */
@@ -259,6 +260,38 @@ kvx_status kvx_unpack_kv_first(const void* send_buf, void* const* layer_bases, i
                                int64_t num_cache_blocks, const int64_t* req_offsets,
                                int32_t num_reqs, const kvx_xfer* xfers, const int64_t* xfer_count,
                                int64_t total_blocks, int32_t* err_flag, hipStream_t stream);
+
+/*
+ * kvx_signal_add / kvx_signal_wait — device-side completion signalling between two streams
+ * ("5. flagcx connector design & dev & test", §1.2, the send path and wait_for_layer_load:
+ * the last transfer of a batch adds to the receiver's signal counter, and the receiver's
+ * stream waits on the GPU until the counter is at least the value it was told to expect).
+ * Used to pipeline a transfer layer by layer: the producer stream packs layer l and then
+ * adds 1; the consumer stream waits for l+1 and then moves layer l on.
+ *   counter     one uint64 in device memory, 8-byte aligned, owned by the caller; it only
+ *               ever grows, so waiting for the largest expected value covers smaller ones.
+ *   kvx_signal_add: once every piece of work enqueued on `stream` before this call has
+ *               finished, atomically adds `delta` to *counter (a device-coherent atomic).
+ *               The kernel boundary in front of it has already made that earlier work's
+ *               writes visible to the whole device, so whoever sees the new count on this
+ *               GPU also sees those writes.
+ *   kvx_signal_wait: work enqueued on `stream` after this call starts only once
+ *               *counter >= value; that work acquires at its own kernel boundary, so it
+ *               reads what the producer wrote before the add. The wait is one wavefront polling the
+ *               counter on the GPU; the host is never blocked. After timeout_us microseconds
+ *               of wall-clock time it gives up, ORs KVX_DEVERR_TIMEOUT into *err_flag (if
+ *               not NULL) and lets the stream go on, so a missing signal cannot keep the
+ *               device busy for ever. timeout_us must be in [1, 60000000].
+ *   Enqueue every add before the wait that expects it (host program order): the two
+ *   streams may then share a hardware queue without waiting on each other in a circle.
+ * Errors: INVALID_ARGUMENT for a NULL counter or a timeout out of range, MISALIGNED for a
+ * counter not 8-byte aligned, KVX_ERR_HIP when the launch (or the wall-clock rate query)
+ * fails.
+ */
+kvx_status kvx_signal_add(uint64_t* counter, uint64_t delta, hipStream_t stream);
+
+kvx_status kvx_signal_wait(const uint64_t* counter, uint64_t value, int64_t timeout_us,
+                           int32_t* err_flag, hipStream_t stream);
 
 #ifdef __cplusplus
 }

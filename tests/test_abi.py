@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "kvx_abi_version", "kvx_build_xfer_list", "kvx_pack", "kvx_reshape_and_cache",
         "kvx_slot_mapping", "kvx_status_string", "kvx_unpack", "kvx_pack_split",
-        "kvx_pack_kv_first", "kvx_unpack_kv_first"])
+        "kvx_pack_kv_first", "kvx_unpack_kv_first", "kvx_signal_add", "kvx_signal_wait"])
 
 
 def test_every_declared_symbol_is_exported(kvx):
@@ -40,7 +40,7 @@ def test_status_strings(kvx):
         s = kvx.kvx_status_string(code)
         assert s.startswith("kvx: ")
     assert "unknown" in kvx.kvx_status_string(99)
-    assert kvx.kvx_abi_version() == 2
+    assert kvx.kvx_abi_version() == 3
 
 
 def test_xfer_struct_size(kvx):
@@ -153,3 +153,16 @@ def test_split_and_kv_first_validation(kvx):
         assert kvf(fn, R=0) == kvx.KVX_ERR_INVALID_ARGUMENT
         assert kvf(fn, buf=P + 16 + 8) == kvx.KVX_ERR_MISALIGNED
         assert kvf(fn, n=0) == kvx.KVX_SUCCESS
+
+
+def test_signal_validation(kvx):
+    assert call(kvx, "kvx_signal_add", None, 1, None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert call(kvx, "kvx_signal_add", P + 4, 1, None) == kvx.KVX_ERR_MISALIGNED
+
+    def wait(counter=P, value=1, timeout=1000):
+        return call(kvx, "kvx_signal_wait", counter, value, timeout, None, None)
+    assert wait(counter=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert wait(timeout=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert wait(timeout=-3) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert wait(timeout=60_000_001) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert wait(counter=P + 12) == kvx.KVX_ERR_MISALIGNED

@@ -1,0 +1,169 @@
+"""GPU tests of the device-side completion signal and of a layer-pipelined transfer.
+
+The signal counter is checked against its definition (a monotone sum of the deltas; a wait
+lets the stream go on exactly when the counter reaches the expected value, or when its
+time runs out). The pipelined transfer — per layer: producer stream packs the layer and adds
+1 to the counter, consumer stream waits for that count and unpacks the layer — must give
+byte for byte what the oracle's pack and unpack give. A bf16 matrix product on the producer
+stream before each layer stands in for that layer's forward pass, so the consumer would run
+ahead of the data if the wait did not hold it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_util import DEV, host_bytes, kvx, layers_from_host, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    log(f"start {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+    log(f"end {request.node.name}")
+
+
+def _busy(n: int, size: int = 4096):
+    """About n bf16 [size x size] products: device work that takes a while, nothing else."""
+    a = torch.ones((size, size), dtype=torch.bfloat16, device=DEV)
+    b = torch.ones((size, size), dtype=torch.bfloat16, device=DEV)
+    c = torch.empty_like(a)
+    for _ in range(n):
+        torch.mm(a, b, out=c)
+    return c
+
+
+def test_signal_add_sums_deltas():
+    K = kvx()
+    counter = torch.zeros(1, dtype=torch.int64, device=DEV)
+    for d in (1, 2, 3, 4, 5):
+        K.kvx_signal_add(counter, d)
+    torch.cuda.synchronize()
+    assert int(counter.item()) == 15
+    # the full 64-bit range: a carry out of the low word
+    counter.fill_((1 << 40) - 1)
+    K.kvx_signal_add(counter, 2)
+    K.kvx_signal_add(counter, (1 << 33))
+    torch.cuda.synchronize()
+    assert int(counter.item()) == (1 << 40) + 1 + (1 << 33)
+
+
+def test_wait_holds_the_stream_until_signalled():
+    K = kvx()
+    prod, cons = torch.cuda.Stream(), torch.cuda.Stream()
+    counter = torch.zeros(1, dtype=torch.int64, device=DEV)
+    marker = torch.zeros(1, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(prod):
+        _busy(150)
+        K.kvx_signal_add(counter, 1)  # enqueued before the wait that expects it
+    with torch.cuda.stream(cons):
+        K.kvx_signal_wait(counter, 1, 20_000_000, err)
+        marker.fill_(7)
+    prod_done, cons_done = prod.query(), cons.query()
+    log(f"right after enqueue: producer done {prod_done}, consumer done {cons_done}")
+    if not prod_done:
+        assert not cons_done, "the consumer finished before the producer's signal"
+    torch.cuda.synchronize()
+    assert int(marker.item()) == 7
+    assert int(err.item()) == 0
+    assert int(counter.item()) == 1
+
+
+def test_wait_on_a_reached_count_passes_at_once():
+    K = kvx()
+    counter = torch.full((1,), 9, dtype=torch.int64, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for v in (0, 1, 9):
+            K.kvx_signal_wait(counter, v, 1_000_000, err)
+        b.record()
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert a.elapsed_time(b) < 100.0  # ms: nowhere near the 1 s limit
+
+
+def test_wait_times_out_and_lets_the_stream_go_on():
+    """The wait's own time limit, set tiny from the host: the counter never reaches 1."""
+    K = kvx()
+    counter = torch.zeros(1, dtype=torch.int64, device=DEV)
+    marker = torch.zeros(1, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        K.kvx_signal_wait(counter, 1, 3000, err)
+        b.record()
+        marker.fill_(5)
+    torch.cuda.synchronize()
+    assert int(err.item()) == K.DEVERR_TIMEOUT
+    assert int(marker.item()) == 5
+    ms = a.elapsed_time(b)
+    log(f"timed-out wait took {ms:.3f} ms (limit 3 ms)")
+    assert 2.5 <= ms < 200.0
+
+
+def _pipelined_roundtrip(seed, L, nb, H, D, lengths, forward_products):
+    K = kvx()
+    case = W.random_transfer(seed, L, nb, 16, H, D, lengths)
+    BB, N = case.src_spec.block_bytes, case.total_blocks
+    src = layers_from_host(case.src_caches, BB)
+    dst = layers_from_host(case.dst_caches, BB)
+    sb, db = K.layer_base_table(src), K.layer_base_table(dst)
+    sid, ro = K.flatten_tables(case.src_tables, DEV)
+    did, _ = K.flatten_tables(case.dst_tables, DEV)
+    xp, cp = K.new_xfer_list(N, DEV)
+    xu, cu = K.new_xfer_list(N, DEV)
+    buf = torch.full((L, max(N, 1), BB), 0x5A, dtype=torch.uint8, device=DEV)
+    counter = torch.zeros(1, dtype=torch.int64, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    werr = torch.zeros(1, dtype=torch.int32, device=DEV)
+    K.kvx_build_xfer_list(sid, None, ro, K.MODE_PACK, xp, cp, err)
+    K.kvx_build_xfer_list(None, did, ro, K.MODE_UNPACK, xu, cu, err)
+    torch.cuda.synchronize()
+    prod, cons = torch.cuda.Stream(), torch.cuda.Stream()
+    for l in range(L):
+        with torch.cuda.stream(prod):
+            if forward_products:
+                _busy(forward_products, 2048)
+            K.kvx_pack(sb[l:l + 1], BB, nb, xp, cp, N, buf[l], err)
+            K.kvx_signal_add(counter, 1)
+        with torch.cuda.stream(cons):
+            K.kvx_signal_wait(counter, l + 1, 20_000_000, werr)
+            K.kvx_unpack([buf[l]], db[l:l + 1], BB, nb, 1, xu, cu, N, err)
+    torch.cuda.synchronize()
+    assert int(werr.item()) == 0
+    assert int(counter.item()) == L
+    exp_buf, e1 = O.pack(case.src_caches, case.src_tables)
+    exp_dst, e2 = O.unpack([exp_buf], case.dst_caches, case.dst_tables)
+    assert int(err.item()) == e1 | e2 == 0
+    if N:
+        assert np.array_equal(host_bytes(buf).reshape(L, N, BB), exp_buf.reshape(L, N, BB))
+    for l in range(L):
+        assert np.array_equal(host_bytes(dst[l]).reshape(nb, BB),
+                              exp_dst[l].view(np.uint8).reshape(nb, BB)), f"layer {l}"
+
+
+@pytest.mark.parametrize("forward_products", [0, 3])
+def test_layer_pipelined_transfer_matches_oracle(forward_products):
+    rng = np.random.default_rng(31)
+    lengths = [int(x) for x in rng.integers(1, 700, size=7)]
+    _pipelined_roundtrip(31, 6, 600, 1, 40, lengths, forward_products)  # 2560 B blocks
+
+
+def test_layer_pipelined_transfer_whole_kib_blocks():
+    """8 KiB blocks (one head of 128 at 16 tokens): the one-batch copy kernels."""
+    rng = np.random.default_rng(32)
+    lengths = [int(x) for x in rng.integers(100, 1500, size=5)]
+    _pipelined_roundtrip(32, 8, 800, 1, 128, lengths, 2)
