@@ -87,7 +87,7 @@ kvx_status kvx_build_xfer_list(const int32_t* src_ids, const int32_t* dst_ids,
     const bool need_src = mode != KVX_MODE_UNPACK, need_dst = mode != KVX_MODE_PACK;
     if ((need_src && !src_ids) || (need_dst && !dst_ids) || !xfers) return KVX_ERR_INVALID_ARGUMENT;
   }
-  if (((uintptr_t)xfers & 7u) != 0) return KVX_ERR_MISALIGNED;
+  if (!aligned16(xfers)) return KVX_ERR_MISALIGNED;
   if (capacity < total_blocks) return KVX_ERR_CAPACITY;
   return from_hip(kvx::launch_build_xfer_list(src_ids, dst_ids, req_offsets, num_reqs,
                                               total_blocks, mode, xfers, xfer_count, err_flag,

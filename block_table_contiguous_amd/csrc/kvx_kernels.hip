@@ -54,6 +54,7 @@ const Tuning& tuning() {
 // --------------------------------------------------------------------------------------
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int64_t i64x2 __attribute__((ext_vector_type(2)));
 #define KVX_GLOBAL __attribute__((address_space(1)))
 // Read-only view of memory no kernel writes while it runs (run list, layer bases, counts):
 // uniform loads through it become scalar loads, which wait on lgkmcnt and so never stall
@@ -465,16 +466,29 @@ __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
   for (int i = 0; i < kScanItems; ++i) {
     const int64_t p = p0 + i;
     if (p < N) {
+      const bool ends = p == N - 1 || st[i + 1];
       if (st[i]) {
-        kvx_xfer* x = out + k;
-        x->src_block = use_src ? sv[i + 1] : p;
-        x->dst_block = use_dst ? dv[i + 1] : p;
-        x->buf_block = p;
-        x->req = rq[i];
+        // a run that starts here: 16-byte stores of (src, dst) and, when it also ends here,
+        // of (buf, num_blocks = 1 | req << 32); the xfer array is 16-byte aligned
+        KVX_GLOBAL i64x2* x = (KVX_GLOBAL i64x2*)(out + k);
+        i64x2 head;
+        head.x = use_src ? (int64_t)sv[i + 1] : p;
+        head.y = use_dst ? (int64_t)dv[i + 1] : p;
+        x[0] = head;
+        if (ends) {
+          i64x2 tail;
+          tail.x = p;
+          tail.y = (int64_t)(((uint64_t)(uint32_t)rq[i] << 32) | 1u);
+          x[1] = tail;
+        } else {
+          out[k].buf_block = p;
+          out[k].req = rq[i];
+        }
         cur = p;
         ++k;
+      } else if (ends) {
+        out[k - 1].num_blocks = (int32_t)(p - cur + 1);
       }
-      if (p == N - 1 || st[i + 1]) out[k - 1].num_blocks = (int32_t)(p - cur + 1);
     }
   }
   carry_cnt += c_tile;

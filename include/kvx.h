@@ -75,7 +75,8 @@ typedef enum kvx_status {
  *   buf_block  position of the run's first block in the flat request-major order of all
  *              listed blocks: (blocks of earlier requests) + index in its block table.
  *              That is where the run sits inside one layer's slice of the send buffer.
- *   num_blocks run length (>= 1); req: the request index. 32 bytes, 8-byte aligned. */
+ *   num_blocks run length (>= 1); req: the request index. 32 bytes; arrays of them are
+ *   16-byte aligned. */
 typedef struct kvx_xfer {
   int64_t src_block;
   int64_t dst_block;
@@ -148,8 +149,9 @@ kvx_status kvx_reshape_and_cache(const void* key, int64_t key_stride_bytes, cons
  *   be NULL). A run breaks at every request start and wherever an addressed side does not
  *   step by +1. Runs are written in request order, then block-table order, to
  *   xfers[0 .. *xfer_count), with buf_block = flat position of the run's first block.
- *   xfers       kvx_xfer [capacity] (output); capacity >= total_blocks is required
- *               (the worst case is one run per block), else KVX_ERR_CAPACITY.
+ *   xfers       kvx_xfer [capacity] (output), 16-byte aligned (else KVX_ERR_MISALIGNED:
+ *               records are written as 16-byte vectors); capacity >= total_blocks is
+ *               required (the worst case is one run per block), else KVX_ERR_CAPACITY.
  *   xfer_count  int64 [1] (output, device): number of runs written.
  * The list is the same for every layer (one block table serves all layers), so one list
  * drives kvx_pack / kvx_unpack for all layers. An invalid req_offsets raises

@@ -105,6 +105,7 @@ def test_build_validation(kvx):
     assert build(cnt=None) == kvx.KVX_ERR_INVALID_ARGUMENT
     assert build(ro=None) == kvx.KVX_ERR_INVALID_ARGUMENT
     assert build(x=P + 4) == kvx.KVX_ERR_MISALIGNED
+    assert build(x=P + 8) == kvx.KVX_ERR_MISALIGNED  # records are written as 16-byte vectors
     assert build(n=-1) == kvx.KVX_ERR_INVALID_ARGUMENT
 
 

@@ -72,6 +72,23 @@ def test_random_roundtrip_geometries(geom):
     run_case(W.random_transfer(int(rng.integers(1 << 30)), 3, nb, bs, H, D, lengths, elem_bytes=e))
 
 
+@pytest.mark.parametrize("latent,elem", [(576, 2), (656, 1)], ids=["latent576-bf16", "latent656-u8"])
+def test_mla_latent_cache_roundtrip(latent, elem):
+    """MLA caches are (blocks, block_size, latent): one latent row per token, no K/V split (the
+    nccl page §2.4 gathers them whole, like blocks-first caches). A block is then 16 * latent *
+    elem bytes: 18 KiB for a 576-wide bf16 latent (whole KiB: the one-batch kernels) and
+    10,496 B for a 656-byte row (not whole KiB: the general kernels). The generator's K/V
+    doubling is folded into the row width, which gives the same block bytes."""
+    bs = 16
+    spec = W.PagedSpec(2, 1, bs, 1, latent // 2, elem)
+    assert spec.block_bytes == bs * latent * elem
+    nb = 1500
+    rng = np.random.default_rng(latent)
+    lengths = [int(x) for x in rng.integers(0, 900, size=11)]
+    lengths[4] = 0
+    run_case(W.random_transfer(latent, 2, nb, bs, 1, latent // 2, lengths, elem_bytes=elem))
+
+
 def test_many_blocks_several_scan_tiles():
     """> 4 tiles of the run-list scan (4096 positions per tile), many requests, empty ones,
     small blocks so every wavefront spans many runs."""
