@@ -411,7 +411,8 @@ def other_workloads(torch, np, W, K, dev, flush, reps):
     out["merge_unpack_asym_tp"] = {
         "workload": "2 sources x 4 of 8 heads, 32 layers x 16 requests x 256 blocks -> [8192][16][K,V][8][128] bf16",
         "bytes": nbytes, "median_ms": round(med, 4), "min_ms": round(mn, 4),
-        "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "traffic": traffic_from_counters("merge_asym_tp", nbytes)}
     # the sender side of the same shapes: full-head caches split into 2 head shards
     xs, cs = K.new_xfer_list(N, dev)
     K.kvx_build_xfer_list(ids, None, ro, K.MODE_PACK, xs, cs)
