@@ -166,6 +166,8 @@ static kvx_status kv_first_checks(void* const* layer_bases, int32_t num_layers,
       total_blocks < 0 || total_blocks > kMaxBlocks || num_reqs < 0)
     return KVX_ERR_INVALID_ARGUMENT;
   if (segment_bytes % 1024 != 0 || !mult16(plane_stride_bytes)) return KVX_ERR_MISALIGNED;
+  // the V plane starts after the K plane's blocks (planes never overlap)
+  if (num_cache_blocks > plane_stride_bytes / segment_bytes) return KVX_ERR_INVALID_ARGUMENT;
   if (num_layers == 0 || total_blocks == 0) return KVX_SUCCESS;
   if (num_reqs == 0 || !layer_bases || !req_offsets || !xfers || !xfer_count || !buffer)
     return KVX_ERR_INVALID_ARGUMENT;

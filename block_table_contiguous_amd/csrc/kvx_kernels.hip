@@ -1228,6 +1228,7 @@ hipError_t launch_kv_first(bool to_buffer, void* const* layer_bases, int32_t num
   a.waves_per_layer = ceil_div(2 * total_blocks * segment_bytes, (int64_t)K * kWaveBytes);
   a.total_waves = a.waves_per_layer * num_layers;
   a.num_wgs = ceil_div(a.total_waves, kCopyWavesPerWg);
+  if (a.num_wgs >= ((int64_t)1 << 31)) return hipErrorInvalidConfiguration;
   a.num_reqs = num_reqs;
   a.num_layers = num_layers;
   a.xcd_remap = tuning().xcd_remap;

@@ -246,6 +246,8 @@ kvx_status kvx_pack_split(void* const* layer_bases, int32_t num_layers, int64_t 
  *   its V segments — exactly what gathering the layer tensor along the block axis with the
  *   request's block ids returns, one contiguous tensor per (request, layer).
  *   req_offsets   int64 [num_reqs+1], the CSR the run list was built from.
+ *   plane_stride_bytes >= num_cache_blocks*segment_bytes (the planes do not overlap), else
+ *   KVX_ERR_INVALID_ARGUMENT.
  *   segment_bytes must be a multiple of 1024 (KVX_ERR_MISALIGNED otherwise): true for any
  *   16-token block with heads*head_dim a multiple of 32 at 2 bytes per element.
  *   Runs: pack needs KVX_MODE_PACK or KVX_MODE_DIRECT; unpack KVX_MODE_UNPACK or

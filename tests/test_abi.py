@@ -149,6 +149,7 @@ def test_split_and_kv_first_validation(kvx):
     for fn in ("kvx_pack_kv_first", "kvx_unpack_kv_first"):
         assert kvf(fn, seg=512) == kvx.KVX_ERR_MISALIGNED
         assert kvf(fn, plane=8) == kvx.KVX_ERR_MISALIGNED
+        assert kvf(fn, plane=4096 * 99) == kvx.KVX_ERR_INVALID_ARGUMENT  # V plane would overlap K
         assert kvf(fn, seg=0) == kvx.KVX_ERR_INVALID_ARGUMENT
         assert kvf(fn, ro=None) == kvx.KVX_ERR_INVALID_ARGUMENT
         assert kvf(fn, R=0) == kvx.KVX_ERR_INVALID_ARGUMENT

@@ -9,7 +9,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_util import DEV, Transfer, check_runs_equal, host_bytes, kvx, log
+from gpu_util import DEV, Transfer, check_runs_equal, host_bytes, kvx, log, to_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.big]
 
@@ -36,12 +36,18 @@ def pages_caches():
 
 
 def _check_transfer(case, src, dst):
-    spec = case.src_spec
     for t in dst:
         W.fill_device_byte_(t)
     tr = Transfer(case, src, dst)
     tr.run()
     log(f"{case.name}: transfer done, checking")
+    _verify(case, tr)
+
+
+def _verify(case, tr):
+    """The run lists, the send buffer and the destination caches against the oracle: three
+    layers in full, every layer on sampled blocks, and untouched blocks still the fill byte."""
+    spec, src, dst = case.src_spec, tr.src, tr.dst
     assert tr.err_bits() == 0
     check_runs_equal(tr.K, tr.xp, tr.cp, O.xfer_list(case.src_tables, case.dst_tables, O.MODE_PACK))
     check_runs_equal(tr.K, tr.xu, tr.cu, O.xfer_list(case.src_tables, case.dst_tables, O.MODE_UNPACK))
@@ -132,3 +138,86 @@ def test_pages_contiguous_kv_first_full(pages_caches):
         assert np.array_equal(host_bytes(bufv[l, g]), want), (l, g)
         assert np.array_equal(host_bytes(dst[l].view(2, nb, seg)[kv, d_id]), want), (l, g, d_id)
     log(f"kv-first: {SAMPLES} sampled segments identical")
+
+
+def test_step_new_token_write_full(pages_caches):
+    """The rest of the benchmark's step at full size: after the contiguous transfer, the
+    receiver's slot mapping for each request's last prompt token (recomputed locally) and the
+    per-layer new-token write of its 256-byte K and V rows into all 48 destination layers, one
+    launch per layer as in the step. Every block that receives a new row is compared with the
+    oracle: the block as the transfer left it (the source block), then the oracle's write."""
+    spec, src, dst = pages_caches
+    case = W.pages_contiguous()
+    for t in dst:
+        W.fill_device_byte_(t)
+    tr = Transfer(case, src, dst)
+    tr.run()
+    K = tr.K
+    L, nb, bs, row = spec.num_layers, spec.num_blocks, spec.block_size, spec.row_bytes
+    R = len(case.dst_tables)
+    table_h = W.pad_table(case.dst_tables, max(len(t) for t in case.dst_tables))
+    req_h = np.arange(R, dtype=np.int32)
+    pos_h = np.array([n - 1 for n in case.lengths], dtype=np.int64)
+    rng = np.random.default_rng(case.seed + 7)
+    new_k = W.bf16_normal_bits(rng, (L, R, row // 2))
+    new_v = W.bf16_normal_bits(rng, (L, R, row // 2))
+    slots = torch.empty(R, dtype=torch.int64, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    K.kvx_slot_mapping(to_dev(table_h), to_dev(req_h), to_dev(pos_h), bs, slots, err)
+    kd, vd = to_dev(new_k), to_dev(new_v)
+    view = dst[0].view(torch.int16).view(nb, bs, 2, spec.num_kv_heads, spec.head_dim)
+    cnb, cbs, bst, tst, kst = K.cache_strides(view)
+    for l in range(L):
+        K.kvx_reshape_and_cache(kd[l], vd[l], slots, dst[l], cnb, cbs, bst, tst, kst, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and tr.err_bits() == 0
+    exp_slots, e = O.slot_mapping(table_h, req_h, pos_h, bs)
+    assert e == 0 and np.array_equal(slots.cpu().numpy(), exp_slots)
+    # the written blocks, gathered into a small cache: block i of it is destination block blocks[i]
+    blocks = sorted(set(int(s) // bs for s in exp_slots))
+    where = {b: i for i, b in enumerate(blocks)}
+    mini_slots = np.array([where[int(s) // bs] * bs + int(s) % bs for s in exp_slots], np.int64)
+    dst_to_src = {int(d): int(s_) for s_, d in zip(np.concatenate(case.src_tables), np.concatenate(case.dst_tables))}
+    for l in range(L):
+        before = np.stack([host_bytes(src[l][dst_to_src[b]]) for b in blocks])
+        exp, e = O.reshape_and_cache(before, new_k[l], new_v[l], mini_slots, len(blocks), bs, bst, tst, kst)
+        assert e == 0
+        got = np.stack([host_bytes(dst[l][b]) for b in blocks]).reshape(-1)
+        assert np.array_equal(got, exp), f"layer {l}"
+    log(f"new-token write: {R} tokens x {L} layers identical")
+
+
+def test_layer_pipelined_transfer_full(pages_caches):
+    """The contiguous transfer layer by layer at full size: per layer, a bf16 product on a
+    forward stream, then on a copy stream that layer's pack and a signal add, and on a
+    consumer stream the signal wait and that layer's unpack. Checked like the one-launch
+    transfer."""
+    spec, src, dst = pages_caches
+    case = W.pages_contiguous()
+    for t in dst:
+        W.fill_device_byte_(t)
+    tr = Transfer(case, src, dst)
+    tr.build()
+    K, L, N, BB, nb = tr.K, spec.num_layers, tr.N, tr.BB, spec.num_blocks
+    tr.buf.fill_(0x5A)
+    bufv = tr.buf.view(L, N, BB)
+    a = torch.full((2048, 2048), 0.5, dtype=torch.bfloat16, device=DEV)
+    c = torch.empty_like(a)
+    counter = torch.zeros(1, dtype=torch.int64, device=DEV)
+    werr = torch.zeros(1, dtype=torch.int32, device=DEV)
+    torch.cuda.synchronize()
+    fwd, cpy, cons = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    evs = [torch.cuda.Event() for _ in range(L)]
+    for l in range(L):
+        with torch.cuda.stream(fwd):
+            torch.mm(a, a, out=c)
+            evs[l].record(fwd)
+        cpy.wait_event(evs[l])
+        K.kvx_pack(tr.src_bases[l:l + 1], BB, nb, tr.xp, tr.cp, N, bufv[l], tr.err, stream=cpy)
+        K.kvx_signal_add(counter, 1, stream=cpy)
+        K.kvx_signal_wait(counter, l + 1, 20_000_000, werr, stream=cons)
+        K.kvx_unpack([bufv[l]], tr.dst_bases[l:l + 1], BB, nb, 1, tr.xu, tr.cu, N, tr.err, stream=cons)
+    torch.cuda.synchronize()
+    assert int(werr.item()) == 0 and int(counter.item()) == L
+    log("layer-pipelined transfer done, checking")
+    _verify(case, tr)
