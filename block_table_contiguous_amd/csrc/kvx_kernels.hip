@@ -94,6 +94,11 @@ constexpr int kCopyWavesPerWg = kCopyThreads / kWave;
 #endif
 // 1 KiB wavefront loads a lane issues before its stores (8 -> 8 KiB in flight per wavefront)
 constexpr int kCopyBatch = KVX_COPY_BATCH;
+#ifndef KVX_WRITE_SLOTS
+#define KVX_WRITE_SLOTS 8
+#endif
+// 1 KiB slots per wavefront in the new-token write
+constexpr int kWriteSlots = KVX_WRITE_SLOTS;
 
 template <bool NT>
 __device__ __forceinline__ u32x4 load16(const char* p) {
@@ -301,7 +306,7 @@ template <bool NTL, bool NTS>
 __global__ __launch_bounds__(256) void write_slots_kernel(WriteArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t w = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
-  const int64_t s0 = w * kCopyBatch;
+  const int64_t s0 = w * kWriteSlots;
   if (s0 >= a.total_slots) return;
   const int64_t row_kib = a.row_bytes / kWaveBytes;
   const int64_t per_tok = 2 * row_kib;
@@ -311,11 +316,11 @@ __global__ __launch_bounds__(256) void write_slots_kernel(WriteArgs a) {
   int64_t piece = within - kv * row_kib;
   const KVX_CONST int64_t* sl = readonly(a.slots);
 
-  const char* sp[kCopyBatch];
-  int64_t tok[kCopyBatch], dof[kCopyBatch];
-  bool live[kCopyBatch];
+  const char* sp[kWriteSlots];
+  int64_t tok[kWriteSlots], dof[kWriteSlots];
+  bool live[kWriteSlots];
 #pragma unroll
-  for (int j = 0; j < kCopyBatch; ++j) {
+  for (int j = 0; j < kWriteSlots; ++j) {
     live[j] = s0 + j < a.total_slots;
     tok[j] = t;
     dof[j] = kv * a.kv_stride + piece * kWaveBytes;  // offset inside the token's slot
@@ -326,18 +331,18 @@ __global__ __launch_bounds__(256) void write_slots_kernel(WriteArgs a) {
       if (++kv == 2) { kv = 0; ++t; }
     }
   }
-  u32x4 v[kCopyBatch];
+  u32x4 v[kWriteSlots];
 #pragma unroll
-  for (int j = 0; j < kCopyBatch; ++j) v[j] = load16<NTL>(sp[j] + lane * kVec);
+  for (int j = 0; j < kWriteSlots; ++j) v[j] = load16<NTL>(sp[j] + lane * kVec);
 
-  char* dp[kCopyBatch];
-  bool on[kCopyBatch];
+  char* dp[kWriteSlots];
+  bool on[kWriteSlots];
   bool bad = false;
   int64_t cur = -1;
   char* base = nullptr;
   bool ok = false;
 #pragma unroll
-  for (int j = 0; j < kCopyBatch; ++j) {
+  for (int j = 0; j < kWriteSlots; ++j) {
     if (live[j] && tok[j] != cur) {
       cur = tok[j];
       const int64_t s = sl[cur];
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(256) void write_slots_kernel(WriteArgs a) {
     dp[j] = base + dof[j];
   }
 #pragma unroll
-  for (int j = 0; j < kCopyBatch; ++j)
+  for (int j = 0; j < kWriteSlots; ++j)
     if (on[j]) store16<NTS>(dp[j] + lane * kVec, v[j]);
   if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_SLOT_RANGE);
 }
@@ -1042,7 +1047,7 @@ hipError_t launch_reshape_and_cache(const void* key, int64_t key_stride, const v
                                     hipStream_t stream) {
   const int64_t total_slots = num_tokens * 2 * (row_bytes / kWaveBytes);
   if (row_bytes % kWaveBytes == 0 && tuning().one_batch &&
-      ceil_div(ceil_div(total_slots, kCopyBatch), 4) < ((int64_t)1 << 31)) {
+      ceil_div(ceil_div(total_slots, kWriteSlots), 4) < ((int64_t)1 << 31)) {
     WriteArgs a;
     a.key = (const char*)key;
     a.value = (const char*)value;
@@ -1059,7 +1064,7 @@ hipError_t launch_reshape_and_cache(const void* key, int64_t key_stride, const v
     a.kv_stride = kv_stride;
     a.total_slots = total_slots;
     a.block_size = block_size;
-    const unsigned grid = (unsigned)ceil_div(ceil_div(total_slots, kCopyBatch), 4);
+    const unsigned grid = (unsigned)ceil_div(ceil_div(total_slots, kWriteSlots), 4);
     switch (tuning().write_nt & 3) {
       case 0: write_slots_kernel<false, false><<<grid, 256, 0, stream>>>(a); break;
       case 1: write_slots_kernel<true, false><<<grid, 256, 0, stream>>>(a); break;
