@@ -297,6 +297,26 @@ def pin_unpack_golden(o):
         assert got == g["dst_tags_after_unpack"][l]
 
 
+def pin_shared_prefix_golden(o):
+    """Two requests sharing prefix blocks: runs in all three modes, the buffer (shared blocks
+    appear once per request) and the receiver's blocks, all worked by hand."""
+    g = _golden("prefix_sharing_hw8.json")
+    src = [np.array(t) for t in g["src_tables"]]
+    dst = [np.array(t) for t in g["dst_tables"]]
+    for mode, key in ((o.MODE_PACK, "runs_pack"), (o.MODE_UNPACK, "runs_unpack"),
+                      (o.MODE_DIRECT, "runs_direct")):
+        assert [list(x) for x in o.xfer_list(src, dst, mode)] == g[key], key
+    nb = g["num_blocks"]
+    buf, err = o.pack(_tagged_caches(2, nb, 16), src)
+    assert err == 0 and buf[:, :, 0].tolist() == g["buffer_tags"]
+    assert np.all(buf == buf[:, :, :1])
+    out, err = o.unpack([buf], [np.full((nb, 16), 0xEE, np.uint8) for _ in range(2)], dst)
+    assert err == 0
+    for l in range(2):
+        got = [None if np.all(out[l][b] == 0xEE) else int(out[l][b][0]) for b in range(nb)]
+        assert got == g["dst_tags_after_unpack"][l]
+
+
 def pin_unpack_equals_index_put(o):
     c = W.random_transfer(22, 2, 200, 4, 2, 4, [13, 0, 50, 7])
     buf, _ = o.pack(c.src_caches, c.src_tables)

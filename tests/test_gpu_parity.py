@@ -89,6 +89,40 @@ def test_mla_latent_cache_roundtrip(latent, elem):
     run_case(W.random_transfer(latent, 2, nb, bs, 1, latent // 2, lengths, elem_bytes=elem))
 
 
+@pytest.mark.parametrize("bs,H,D,contiguous", [(16, 1, 128, True), (16, 3, 40, False)],
+                         ids=["8KiB-shared-run", "7680B-shared-scattered"])
+def test_shared_prefix_transfer(bs, H, D, contiguous):
+    """Prefix sharing (the v1 diagram's prefix-cache toy at scale): 9 requests whose tables all
+    start with the same 37 cached blocks, then blocks of their own. The shared blocks are read
+    once per request; every request gets fresh receiver blocks."""
+    rng = np.random.default_rng(bs * 1000 + D)
+    L, nb = 3, 2000
+    spec = W.PagedSpec(L, nb, bs, H, D)
+    if contiguous:
+        shared = np.arange(500, 537)
+        pool = rng.permutation(np.setdiff1d(np.arange(nb), shared))
+    else:
+        perm = rng.permutation(nb)
+        shared, pool = perm[:37], perm[37:]
+    counts = [int(x) for x in rng.integers(0, 60, size=9)]
+    counts[2] = 0
+    src_tables, k = [], 0
+    for c in counts:
+        src_tables.append(np.concatenate([shared, pool[k:k + c]]).astype(np.int32))
+        k += c
+    dst_pool = rng.permutation(nb)
+    dst_tables, k = [], 0
+    for t in src_tables:
+        dst_tables.append(dst_pool[k:k + len(t)].astype(np.int32))
+        k += len(t)
+    words = spec.block_bytes // 2
+    case = W.TransferCase("shared-prefix", spec, spec, [len(t) * bs for t in src_tables], src_tables,
+                          dst_tables, 0,
+                          src_caches=[W.random_words(rng, (nb, words)) for _ in range(L)],
+                          dst_caches=[np.full((nb, words), W.SENTINEL16, np.uint16) for _ in range(L)])
+    run_case(case)
+
+
 def test_many_blocks_several_scan_tiles():
     """> 4 tiles of the run-list scan (4096 positions per tile), many requests, empty ones,
     small blocks so every wavefront spans many runs."""
