@@ -124,14 +124,26 @@ def test_shared_prefix_transfer(bs, H, D, contiguous):
 
 
 def test_many_blocks_several_scan_tiles():
-    """> 4 tiles of the run-list scan (4096 positions per tile), many requests, empty ones,
+    """> 4 tiles of the run-list scan (8192 positions per tile), many requests, empty ones,
     small blocks so every wavefront spans many runs."""
     rng = np.random.default_rng(77)
-    lengths = [int(x) for x in rng.integers(0, 160, size=1000)]
+    lengths = [int(x) for x in rng.integers(0, 320, size=1000)]
     for i in range(0, 1000, 37):
         lengths[i] = 0
-    case = W.random_transfer(78, 2, 60000, 4, 1, 8, lengths, run_p=0.3)
-    assert case.total_blocks > 4 * 4096
+    case = W.random_transfer(78, 2, 120000, 4, 1, 8, lengths, run_p=0.3)
+    assert case.total_blocks > 4 * 8192
+    run_case(case)
+
+
+def test_offsets_beyond_the_lds_stage():
+    """5000 requests: past the 4096 request offsets the run builder stages in LDS, so it reads
+    them from global memory; a third of the requests are empty."""
+    rng = np.random.default_rng(79)
+    lengths = [int(x) for x in rng.integers(0, 40, size=5000)]
+    for i in range(0, 5000, 3):
+        lengths[i] = 0
+    case = W.random_transfer(80, 1, 40000, 4, 1, 8, lengths, run_p=0.4)
+    assert len(case.src_tables) >= 4096
     run_case(case)
 
 
@@ -230,6 +242,43 @@ def test_slot_mapping_golden_and_errors():
                                    case["block_size"])
         assert out.cpu().numpy().tolist() == exp.tolist(), case["name"]
         assert int(err.item()) == eerr, case["name"]
+
+
+def test_slot_mapping_positions_past_32_bits():
+    """Positions and slots beyond 2^31 take the kernels' 64-bit division: blocks of 2^30
+    slots, positions up to 3 * 2^30 - 1."""
+    K = kvx()
+    bs = 1 << 30
+    table = np.array([[7, 9, 11], [4, -1, 2]], np.int32)
+    req = np.array([0, 0, 0, 1, 1, 1, 0], np.int32)
+    pos = np.array([(1 << 31) + 5, 3 * bs - 1, 0, bs + 1, 2 * bs + 17, (1 << 31) - 1, 3 * bs], np.int64)
+    slots = torch.empty(len(req), dtype=torch.int64, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    K.kvx_slot_mapping(to_dev(table), to_dev(req), to_dev(pos), bs, slots, err)
+    torch.cuda.synchronize()
+    exp, e = O.slot_mapping(table, req, pos, bs)
+    assert np.array_equal(slots.cpu().numpy(), exp)
+    assert int(err.item()) == e == O.DEVERR_TABLE_RANGE
+
+
+@pytest.mark.parametrize("row", [256, 1024], ids=["general", "whole-KiB"])
+def test_reshape_and_cache_slots_past_32_bits(row):
+    """Slots beyond 2^31 (blocks of 2^30 slots, only the first few used) in both write kernels."""
+    K = kvx()
+    bs, nb, bst, tst, kst = 1 << 30, 3, 64 << 10, 2 * row, row
+    slots_h = np.array([2 * bs + 5, 3, bs + 7, -1, 3 * bs + 1, 2 * bs + 6], np.int64)
+    T = len(slots_h)
+    rng = np.random.default_rng(row)
+    key = W.random_words(rng, (T, row // 2))
+    val = W.random_words(rng, (T, row // 2))
+    cache_h = np.full(nb * bst // 2, W.SENTINEL16, np.uint16)
+    cache = to_dev(cache_h)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    K.kvx_reshape_and_cache(to_dev(key), to_dev(val), to_dev(slots_h), cache, nb, bs, bst, tst, kst, err)
+    torch.cuda.synchronize()
+    exp, e = O.reshape_and_cache(cache_h, key, val, slots_h, nb, bs, bst, tst, kst)
+    assert np.array_equal(host_bytes(cache), exp)
+    assert int(err.item()) == e == O.DEVERR_SLOT_RANGE
 
 
 def test_slot_mapping_decode_workload():
