@@ -374,13 +374,17 @@ __global__ __launch_bounds__(256) void write_slots_kernel(WriteArgs a) {
 }
 
 // --------------------------------------------------------------------------------------
-// a3 — transfer list: run-start flags -> workgroup prefix scan -> compaction
+// a3 — transfer list: run-start flags -> prefix scan -> compaction, one tile per workgroup
 // --------------------------------------------------------------------------------------
 
-constexpr int kScanThreads = 512;
-constexpr int kScanItems = 16;
-constexpr int kScanTile = kScanThreads * kScanItems;
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 8;                          // positions per thread in the own tile
+constexpr int kScanTile = kScanThreads * kScanItems;   // 2048 positions per workgroup
 constexpr int kScanWaves = kScanThreads / kWave;
+#ifndef KVX_PREFIX_GROUPS
+#define KVX_PREFIX_GROUPS 4
+#endif
+constexpr int kPrefixGroups = KVX_PREFIX_GROUPS;       // 1024-position groups per prefix round
 constexpr int kLdsOffsets = 4096;  // request offsets staged in LDS when num_reqs < this
 
 // Largest r in [0, R) with ro[r] <= p (0 if none).
@@ -395,37 +399,35 @@ __device__ __forceinline__ int32_t find_request(P ro, int32_t R, int64_t p) {
   return lo;
 }
 
-// One tile of positions [tile, tile + kScanTile): every thread flags run starts among its
-// kScanItems consecutive positions (loading one id before and one after them), a wave scan
-// (shuffles) plus a 16-entry LDS pass turns the flags into run indices, and each thread
-// writes the runs it starts and the lengths of the runs it ends. The scan carries two
-// quantities: the number of starts so far (the run index) and the position of the latest
-// start (for run lengths), so no thread ever reads another thread's output.
-template <class P>
-__device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
-                                           const int32_t* __restrict__ dst, P ro, int32_t R,
-                                           int64_t N, bool use_src, bool use_dst, int64_t tile,
-                                           kvx_xfer* __restrict__ out, int64_t* s_cnt,
-                                           int64_t* s_last, int64_t& carry_cnt,
-                                           int64_t& carry_last) {
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wid = tid / kWave;
-  const int64_t p0 = tile + (int64_t)tid * kScanItems;
-  int32_t sv[kScanItems + 2], dv[kScanItems + 2];  // ids at p0-1 .. p0+kScanItems
+// Ids at positions p0 - 1 .. p0 + ITEMS, loaded unconditionally (indices clamped into
+// [0, N), N > 0) so that all the loads of a round are in flight together.
+template <int ITEMS>
+__device__ __forceinline__ void chunk_ids(const int32_t* __restrict__ src,
+                                          const int32_t* __restrict__ dst, int64_t N,
+                                          bool use_src, bool use_dst, int64_t p0,
+                                          int32_t (&sv)[ITEMS + 2], int32_t (&dv)[ITEMS + 2]) {
 #pragma unroll
-  for (int i = 0; i < kScanItems + 2; ++i) {
-    const int64_t p = p0 - 1 + i;
-    const bool in = p >= 0 && p < N;
-    sv[i] = (use_src && in) ? src[p] : 0;
-    dv[i] = (use_dst && in) ? dst[p] : 0;
+  for (int i = 0; i < ITEMS + 2; ++i) {
+    int64_t p = p0 - 1 + i;
+    p = p < 0 ? 0 : (p < N ? p : N - 1);
+    sv[i] = use_src ? src[p] : 0;
+    dv[i] = use_dst ? dst[p] : 0;
   }
+}
+
+// Run-start flags of positions p0 .. p0 + ITEMS (one past the chunk, for run ends) and the
+// request of each of the first ITEMS, from the ids chunk_ids loaded. Position p starts a run
+// if it is the first position, the first of its request, or an addressed side does not step
+// by +1 from p - 1. Positions at or past N are not starts.
+template <int ITEMS, class P>
+__device__ __forceinline__ void chunk_flags(P ro, int32_t R, int64_t N, bool use_src,
+                                            bool use_dst, int64_t p0,
+                                            const int32_t (&sv)[ITEMS + 2],
+                                            const int32_t (&dv)[ITEMS + 2],
+                                            bool (&st)[ITEMS + 1], int32_t (&rq)[ITEMS]) {
   int32_t r = (p0 < N) ? find_request(ro, R, p0) : 0;
-  bool st[kScanItems + 1];
-  int32_t rq[kScanItems];
-  int64_t cnt = 0, last = -1;
 #pragma unroll
-  for (int i = 0; i <= kScanItems; ++i) {
+  for (int i = 0; i <= ITEMS; ++i) {
     const int64_t p = p0 + i;
     bool f = false;
     if (p < N) {
@@ -435,11 +437,93 @@ __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
           (use_dst && (int64_t)dv[i + 1] != (int64_t)dv[i] + 1);
     }
     st[i] = f;
-    if (i < kScanItems) {
-      rq[i] = r;
-      if (f) { ++cnt; last = p; }
+    if (i < ITEMS) rq[i] = r;
+  }
+}
+
+// Workgroup b owns positions [b * kScanTile, (b + 1) * kScanTile). It first counts the run
+// starts before its tile and finds the latest of them (a pass over every earlier id and over
+// the request offsets, no writes), then flags its own positions (8 per
+// thread), turns them into run indices and latest-start positions with a wave scan plus a
+// 4-entry LDS pass, and writes the runs each thread starts and the lengths of the runs it
+// ends. No thread reads another's output, and no workgroup waits for another. Request
+// offsets are staged in LDS when there are fewer than kLdsOffsets requests.
+template <class P>
+__device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
+                                           const int32_t* __restrict__ dst, P ro, int32_t R,
+                                           int64_t N, bool use_src, bool use_dst,
+                                           kvx_xfer* __restrict__ out, int64_t* __restrict__ count,
+                                           int64_t* s_cnt, int64_t* s_last) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  const int64_t tile = (int64_t)blockIdx.x * kScanTile;
+
+  // 1. run starts before the tile: count and latest position. With a valid CSR a position
+  //    p in [1, tile) starts a run iff its ids break the +1 step from p - 1 or a request
+  //    starts at p, so the count is: position 0, plus the id breaks, plus the request starts
+  //    that are not id breaks. (a) streams the ids in rounds of kPrefixGroups groups of
+  //    kScanThreads * 4 positions, 4 consecutive positions per lane; (b) walks the offsets.
+  int64_t pc = 0, pl = -1;
+  if (tile > 0) {
+    for (int64_t base = 0; base < tile; base += (int64_t)kScanThreads * 4 * kPrefixGroups) {
+      int32_t sv[kPrefixGroups][6], dv[kPrefixGroups][6];
+#pragma unroll
+      for (int g = 0; g < kPrefixGroups; ++g)
+        chunk_ids<4>(src, dst, N, use_src, use_dst, base + ((int64_t)g * kScanThreads + tid) * 4,
+                     sv[g], dv[g]);
+#pragma unroll
+      for (int g = 0; g < kPrefixGroups; ++g) {
+        const int64_t q0 = base + ((int64_t)g * kScanThreads + tid) * 4;  // never straddles the tile
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t p = q0 + i;
+          const bool brk = (use_src && (int64_t)sv[g][i + 1] != (int64_t)sv[g][i] + 1) ||
+                           (use_dst && (int64_t)dv[g][i + 1] != (int64_t)dv[g][i] + 1);
+          if (p >= 1 && p < tile && brk) { ++pc; pl = p; }
+        }
+      }
+    }
+    for (int32_t r = 1 + tid; r < R; r += kScanThreads) {
+      const int64_t q = ro[r];
+      if (q >= 1 && q < tile && q != ro[r - 1]) {  // the first request starting at q
+        pl = q > pl ? q : pl;
+        const bool brk = (use_src && (int64_t)src[q] != (int64_t)src[q - 1] + 1) ||
+                         (use_dst && (int64_t)dst[q] != (int64_t)dst[q - 1] + 1);
+        if (!brk) ++pc;
+      }
+    }
+    if (tid == 0) {  // position 0
+      ++pc;
+      pl = pl > 0 ? pl : 0;
     }
   }
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    pc += __shfl_xor(pc, d, kWave);
+    const int64_t o = __shfl_xor(pl, d, kWave);
+    pl = o > pl ? o : pl;
+  }
+  if (lane == 0) { s_cnt[wid] = pc; s_last[wid] = pl; }
+  __syncthreads();
+  int64_t carry_cnt = 0, carry_last = -1;
+#pragma unroll
+  for (int w = 0; w < kScanWaves; ++w) {
+    carry_cnt += s_cnt[w];
+    carry_last = s_last[w] > carry_last ? s_last[w] : carry_last;
+  }
+  __syncthreads();
+
+  // 2. the own tile
+  const int64_t p0 = tile + (int64_t)tid * kScanItems;
+  bool st[kScanItems + 1];
+  int32_t rq[kScanItems], sv[kScanItems + 2], dv[kScanItems + 2];
+  if (N > 0) chunk_ids<kScanItems>(src, dst, N, use_src, use_dst, p0, sv, dv);
+  chunk_flags<kScanItems>(ro, R, N, use_src, use_dst, p0, sv, dv, st, rq);
+  int64_t cnt = 0, last = -1;
+#pragma unroll
+  for (int i = 0; i < kScanItems; ++i)
+    if (st[i]) { ++cnt; last = p0 + i; }
 
   // workgroup scan of (cnt: sum, last: max)
   int64_t ci = cnt, li = last;
@@ -453,15 +537,13 @@ __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
   if (lane == 0) li_excl = -1;
   if (lane == kWave - 1) { s_cnt[wid] = ci; s_last[wid] = li; }
   __syncthreads();
-  int64_t c_before = 0, l_before = -1, c_tile = 0, l_tile = -1;
+  int64_t c_before = 0, l_before = -1, c_tile = 0;
 #pragma unroll
   for (int w = 0; w < kScanWaves; ++w) {
     const int64_t c = s_cnt[w], l = s_last[w];
     if (w < wid) { c_before += c; l_before = l > l_before ? l : l_before; }
     c_tile += c;
-    l_tile = l > l_tile ? l : l_tile;
   }
-  __syncthreads();
 
   int64_t k = carry_cnt + c_before + (ci - cnt);
   int64_t cur = carry_last;
@@ -472,6 +554,7 @@ __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
     const int64_t p = p0 + i;
     if (p < N) {
       const bool ends = p == N - 1 || st[i + 1];
+      if (k >= N) break;  // only with offsets that are not a CSR (flagged by workgroup 0)
       if (st[i]) {
         // a run that starts here: 16-byte stores of (src, dst) and, when it also ends here,
         // of (buf, num_blocks = 1 | req << 32); the xfer array is 16-byte aligned
@@ -496,13 +579,9 @@ __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
       }
     }
   }
-  carry_cnt += c_tile;
-  if (l_tile > carry_last) carry_last = l_tile;
+  if (blockIdx.x == gridDim.x - 1 && tid == 0) *count = carry_cnt + c_tile;
 }
 
-// A single workgroup of 512 threads walks the blocks tile by tile (8192 positions per tile).
-// When there are fewer than 4096 requests their offsets are staged in LDS first, so the
-// per-position request lookups never wait on global memory.
 __global__ __launch_bounds__(kScanThreads) void build_xfer_kernel(
     const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
     const int64_t* __restrict__ ro, int32_t R, int64_t N, int32_t mode,
@@ -514,26 +593,22 @@ __global__ __launch_bounds__(kScanThreads) void build_xfer_kernel(
   const bool use_src = mode != KVX_MODE_UNPACK;
   const bool use_dst = mode != KVX_MODE_PACK;
   const bool in_lds = R < kLdsOffsets;
+  const bool check = blockIdx.x == 0;  // one workgroup checks the CSR
 
   // CSR sanity: ro[0] == 0, non-decreasing, ro[R] == N
-  for (int32_t i = tid; i <= R; i += kScanThreads) {
-    const int64_t v = ro[i];
-    if (in_lds) s_ro[i] = v;
-    if (i < R && ro[i + 1] < v) raise_error(err, KVX_DEVERR_OFFSETS);
+  if (in_lds || check) {
+    for (int32_t i = tid; i <= R; i += kScanThreads) {
+      const int64_t v = ro[i];
+      if (in_lds) s_ro[i] = v;
+      if (check && i < R && ro[i + 1] < v) raise_error(err, KVX_DEVERR_OFFSETS);
+    }
   }
-  if (tid == 0 && (ro[0] != 0 || ro[R] != N)) raise_error(err, KVX_DEVERR_OFFSETS);
+  if (check && tid == 0 && (ro[0] != 0 || ro[R] != N)) raise_error(err, KVX_DEVERR_OFFSETS);
   __syncthreads();
-
-  int64_t carry_cnt = 0, carry_last = -1;
-  for (int64_t tile = 0; tile < N; tile += kScanTile) {
-    if (in_lds)
-      build_tile<const int64_t*>(src, dst, s_ro, R, N, use_src, use_dst, tile, out, s_cnt, s_last,
-                                 carry_cnt, carry_last);
-    else
-      build_tile<const int64_t*>(src, dst, ro, R, N, use_src, use_dst, tile, out, s_cnt, s_last,
-                                 carry_cnt, carry_last);
-  }
-  if (tid == 0) *count = carry_cnt;
+  if (in_lds)
+    build_tile<const int64_t*>(src, dst, s_ro, R, N, use_src, use_dst, out, count, s_cnt, s_last);
+  else
+    build_tile<const int64_t*>(src, dst, ro, R, N, use_src, use_dst, out, count, s_cnt, s_last);
 }
 
 // --------------------------------------------------------------------------------------
@@ -1085,8 +1160,9 @@ hipError_t launch_build_xfer_list(const int32_t* src_ids, const int32_t* dst_ids
                                   const int64_t* req_offsets, int32_t num_reqs,
                                   int64_t total_blocks, int32_t mode, kvx_xfer* xfers,
                                   int64_t* xfer_count, int32_t* err, hipStream_t stream) {
-  build_xfer_kernel<<<1, kScanThreads, 0, stream>>>(src_ids, dst_ids, req_offsets, num_reqs,
-                                                    total_blocks, mode, xfers, xfer_count, err);
+  const int64_t tiles = total_blocks > 0 ? ceil_div(total_blocks, kScanTile) : 1;
+  build_xfer_kernel<<<(unsigned)tiles, kScanThreads, 0, stream>>>(
+      src_ids, dst_ids, req_offsets, num_reqs, total_blocks, mode, xfers, xfer_count, err);
   return hipGetLastError();
 }
 
