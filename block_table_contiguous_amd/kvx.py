@@ -130,6 +130,16 @@ def _want(t, dtype, name):
         raise ValueError(f"kvx: {name} must be contiguous")
 
 
+def _want_runs(xfers, xfer_count, total_blocks: int):
+    """A run list the copy kernels may read up to total_blocks records of."""
+    import torch
+
+    _want(xfers, torch.int64, "xfers")
+    _want(xfer_count, torch.int64, "xfer_count")
+    if xfers.numel() // 4 < total_blocks or xfer_count.numel() < 1:
+        raise ValueError("kvx: the run list holds fewer than total_blocks records")
+
+
 def layer_base_table(layers: Sequence, device=None):
     """Device int64 array of the layers' base addresses (the per-layer cache pointers the
     pack/unpack kernels index)."""
@@ -256,6 +266,7 @@ def kvx_pack(layer_bases, block_bytes: int, num_cache_blocks: int, xfers, xfer_c
     import torch
 
     _want(layer_bases, torch.int64, "layer_bases")
+    _want_runs(xfers, xfer_count, total_blocks)
     L = layer_bases.numel()
     if send_buf.numel() * send_buf.element_size() < L * total_blocks * block_bytes:
         raise ValueError("kvx: send_buf smaller than num_layers * total_blocks * block_bytes")
@@ -273,6 +284,7 @@ def kvx_unpack(send_bufs: Sequence, layer_bases, block_bytes: int, num_cache_blo
     import torch
 
     _want(layer_bases, torch.int64, "layer_bases")
+    _want_runs(xfers, xfer_count, total_blocks)
     L = layer_bases.numel()
     S = len(send_bufs)
     if not 1 <= S <= MAX_SOURCES:
@@ -295,6 +307,7 @@ def kvx_pack_split(layer_bases, block_bytes: int, num_cache_blocks: int, rows_pe
     import torch
 
     _want(layer_bases, torch.int64, "layer_bases")
+    _want_runs(xfers, xfer_count, total_blocks)
     L = layer_bases.numel()
     D = len(send_bufs)
     if not 1 <= D <= MAX_SOURCES:
@@ -316,6 +329,7 @@ def kvx_pack_kv_first(layer_bases, segment_bytes: int, plane_stride_bytes: int, 
     import torch
 
     _want(layer_bases, torch.int64, "layer_bases")
+    _want_runs(xfers, xfer_count, total_blocks)
     _want(req_offsets, torch.int64, "req_offsets")
     L = layer_bases.numel()
     if send_buf.numel() * send_buf.element_size() < L * 2 * total_blocks * segment_bytes:
@@ -334,6 +348,7 @@ def kvx_unpack_kv_first(send_buf, layer_bases, segment_bytes: int, plane_stride_
     import torch
 
     _want(layer_bases, torch.int64, "layer_bases")
+    _want_runs(xfers, xfer_count, total_blocks)
     _want(req_offsets, torch.int64, "req_offsets")
     L = layer_bases.numel()
     if send_buf.numel() * send_buf.element_size() < L * 2 * total_blocks * segment_bytes:

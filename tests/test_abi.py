@@ -168,3 +168,22 @@ def test_signal_validation(kvx):
     assert wait(timeout=-3) == kvx.KVX_ERR_INVALID_ARGUMENT
     assert wait(timeout=60_000_001) == kvx.KVX_ERR_INVALID_ARGUMENT
     assert wait(counter=P + 12) == kvx.KVX_ERR_MISALIGNED
+
+
+def test_binding_rejects_undersized_tensors(kvx):
+    """The binding checks sizes the C ABI cannot see, before any pointer is taken."""
+    import torch
+    bases = torch.zeros(2, dtype=torch.int64)
+    x, c = torch.zeros((9, 4), dtype=torch.int64), torch.zeros(1, dtype=torch.int64)
+    buf = torch.zeros(2 * 10 * 64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="run list"):
+        kvx.kvx_pack(bases, 64, 100, x, c, 10, buf)  # 9 records for 10 blocks
+    with pytest.raises(ValueError, match="run list"):
+        kvx.kvx_unpack([buf], bases, 64, 100, 1, x, c, 10)
+    x10 = torch.zeros((10, 4), dtype=torch.int64)
+    with pytest.raises(ValueError, match="send_buf smaller"):
+        kvx.kvx_pack(bases, 64, 100, x10, c, 10, buf[:-16])
+    with pytest.raises(ValueError, match="send buffer is smaller"):
+        kvx.kvx_unpack([buf, buf[:100]], bases, 64, 100, 2, x10, c, 10)
+    with pytest.raises(TypeError):
+        kvx.kvx_pack(bases, 64, 100, x10.int(), c, 10, buf)
