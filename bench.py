@@ -258,8 +258,10 @@ def main():
         out_ops[n]["frac_of_peak"] = round(copy_bytes / (kern[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         out_ops[n]["traffic"] = traffic_from_counters(f"{n}_{case.name}", copy_bytes)
     runs_pack, runs_unpack = int(cp.item()), int(cu.item())
-    out_ops["build_pack"]["runs"] = runs_pack
-    out_ops["build_unpack"]["runs"] = runs_unpack
+    for n, runs in (("build_pack", runs_pack), ("pack", runs_pack * L),
+                    ("build_unpack", runs_unpack), ("unpack", runs_unpack * L)):
+        out_ops[n]["runs"] = runs  # descriptors the op reads or writes (per layer for the copies)
+        out_ops[n]["ns_per_run"] = round(kern[n] * 1e6 / max(runs, 1), 2)
 
     if not args.no_ops:
         flush = Flush(torch, dev)
