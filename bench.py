@@ -257,6 +257,9 @@ def main():
         out_ops[n]["GB/s"] = round(copy_bytes / (kern[n] * 1e-3) / 1e9, 1)
         out_ops[n]["frac_of_peak"] = round(copy_bytes / (kern[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         out_ops[n]["traffic"] = traffic_from_counters(f"{n}_{case.name}", copy_bytes)
+    e2e = [a.elapsed_time(b) for (a, _), (_, b) in zip(ev["build_pack"], ev["pack"])]
+    out_ops["build_plus_pack"] = {"avg_ms": round(sum(e2e) / len(e2e), 5),
+                                  "about": "start of the run-list build to the end of the pack, same steps"}
     runs_pack, runs_unpack = int(cp.item()), int(cu.item())
     for n, runs in (("build_pack", runs_pack), ("pack", runs_pack * L),
                     ("build_unpack", runs_unpack), ("unpack", runs_unpack * L)):
