@@ -31,6 +31,11 @@ MUTANTS = [
     ("order_requests_reversed", "    for r, t in enumerate(tables):\n        for j in range(len(t)):\n            order.append((r, j, p))",
      "    for r, t in reversed(list(enumerate(tables))):\n        for j in range(len(t)):\n            order.append((r, j, p))"),
     ("pack_layer0_only", "buf[l, p] = caches[l][b]", "buf[l, p] = caches[0][b]"),
+    ("pack_dedups_shared_blocks", "            buf[l, p] = caches[l][b]\n    return buf, err",
+     "            if any(int(src_tables[rr][jj]) == b for rr, jj, pp in order if pp < p):\n                continue\n"
+     "            buf[l, p] = caches[l][b]\n    return buf, err"),
+    ("runs_direct_ignores_dst", "                if uses_dst and dst[k] != dst[k - 1] + 1:",
+     "                if uses_dst and not uses_src and dst[k] != dst[k - 1] + 1:"),
     ("pack_no_range_check", "if b < 0 or b >= nb:", "if b >= nb:"),
     ("unpack_to_position", "out[l][d] = bufs[0][l, p]", "out[l][p % nb] = bufs[0][l, p]"),
     ("unpack_layer_swap", "out[l][d] = bufs[0][l, p]", "out[l][d] = bufs[0][L - 1 - l, p]"),
