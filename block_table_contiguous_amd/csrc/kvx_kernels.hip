@@ -1178,20 +1178,23 @@ static int64_t blocks_per_wave_for(int64_t wave_bytes, int64_t block_bytes, int6
 }
 
 // Runtime (cache policy, batch) -> template instance. LAUNCH(NTL, NTS, K) launches one.
-#define KVX_POLICY_SWITCH(NT, K, LAUNCH)          \
-  switch (((NT) & 3) * 2 + ((K) <= 4 ? 0 : 1)) { \
-    case 0: LAUNCH(false, false, 4) break;        \
-    case 1: LAUNCH(false, false, 8) break;        \
-    case 2: LAUNCH(true, false, 4) break;         \
-    case 3: LAUNCH(true, false, 8) break;         \
-    case 4: LAUNCH(false, true, 4) break;         \
-    case 5: LAUNCH(false, true, 8) break;         \
-    case 6: LAUNCH(true, true, 4) break;          \
-    default: LAUNCH(true, true, 8) break;         \
+#ifndef KVX_SMALL_BATCH
+#define KVX_SMALL_BATCH 4
+#endif
+#define KVX_POLICY_SWITCH(NT, K, LAUNCH)                       \
+  switch (((NT) & 3) * 2 + ((K) <= KVX_SMALL_BATCH ? 0 : 1)) { \
+    case 0: LAUNCH(false, false, KVX_SMALL_BATCH) break;       \
+    case 1: LAUNCH(false, false, 8) break;                     \
+    case 2: LAUNCH(true, false, KVX_SMALL_BATCH) break;        \
+    case 3: LAUNCH(true, false, 8) break;                      \
+    case 4: LAUNCH(false, true, KVX_SMALL_BATCH) break;        \
+    case 5: LAUNCH(false, true, 8) break;                      \
+    case 6: LAUNCH(true, true, KVX_SMALL_BATCH) break;         \
+    default: LAUNCH(true, true, 8) break;                      \
   }
 
 // Batch of the one-batch kernels: 4 or 8 KiB per wavefront.
-static int batch_of(const CopyTuning& ct) { return ct.batch <= 4 ? 4 : 8; }
+static int batch_of(const CopyTuning& ct) { return ct.batch <= KVX_SMALL_BATCH ? KVX_SMALL_BATCH : 8; }
 
 // The one-batch fast path needs whole-KiB rows and a grid that fits 32-bit workgroup ids.
 static bool use_slots(bool whole_kib, int64_t num_layers, int64_t layer_bytes, int64_t unit) {
