@@ -20,6 +20,7 @@ from .kv_oracle import (  # noqa: F401
     MODE_PACK,
     MODE_UNPACK,
     buffer_order,
+    copy_direct,
     pack,
     pack_kv_first,
     pack_split,

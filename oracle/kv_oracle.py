@@ -278,6 +278,35 @@ def unpack(src_buffers: Sequence[np.ndarray], dst_caches: Sequence[np.ndarray],
     return out, err
 
 
+def copy_direct(src_caches: Sequence[np.ndarray], dst_caches: Sequence[np.ndarray],
+                src_tables: Sequence[np.ndarray], dst_tables: Sequence[np.ndarray]
+                ) -> Tuple[List[np.ndarray], int]:
+    """Move every listed block straight from the sender's cache into the receiver's, with no
+    send buffer in between: for every layer l and table entry (r, j), destination block
+    dst_tables[r][j] of layer l gets source block src_tables[r][j] of layer l. [pd] §四 4.2
+    (_build_transfer_params / batch_transfer_sync_write: one write per source address,
+    destination address and length, from the prefill cache into the decode cache); [pd]
+    §七 item 3 (address = layer base + block length x block id).
+
+    Reading: an entry whose source or destination id is outside its cache is not copied
+    and raises DEVERR_BLOCK_RANGE (pack's rule for sources, unpack's for destinations).
+    Returns (new destination caches as [num_blocks][block_bytes] uint8, error bits).
+    """
+    srcs = [_as_block_bytes(c) for c in src_caches]
+    out = [_as_block_bytes(c).copy() for c in dst_caches]
+    nbs, nbd = srcs[0].shape[0], out[0].shape[0]
+    err = 0
+    for l in range(len(out)):
+        for r in range(len(src_tables)):
+            for j in range(len(src_tables[r])):
+                s, d = int(src_tables[r][j]), int(dst_tables[r][j])
+                if s < 0 or s >= nbs or d < 0 or d >= nbd:
+                    err |= DEVERR_BLOCK_RANGE
+                    continue
+                out[l][d] = srcs[l][s]
+    return out, err
+
+
 # ---------------------------------------------------------------------------------------
 # f1 — kv-first caches: (K/V plane, blocks, block_size, heads, head_dim)
 # ---------------------------------------------------------------------------------------

@@ -317,6 +317,44 @@ def pin_shared_prefix_golden(o):
         assert got == g["dst_tags_after_unpack"][l]
 
 
+def pin_direct_golden(o):
+    """A direct cache-to-cache transfer leaves the receiver's blocks exactly as pack then
+    unpack does, for both hand-worked cases (HW4 and the shared-prefix HW8)."""
+    for name in ("transfer_hw4.json", "prefix_sharing_hw8.json"):
+        g = _golden(name)
+        nb = g["num_blocks"]
+        src = [np.array(t) for t in g["src_tables"]]
+        dst = [np.array(t) for t in g["dst_tables"]]
+        out, err = o.copy_direct(_tagged_caches(2, nb, 16), [np.full((nb, 16), 0xEE, np.uint8)] * 2,
+                                 src, dst)
+        assert err == 0
+        for l in range(2):
+            got = [None if np.all(out[l][b] == 0xEE) else int(out[l][b][0]) for b in range(nb)]
+            assert got == g["dst_tags_after_unpack"][l], name
+
+
+def pin_direct_equals_pack_then_unpack(o):
+    for seed in range(3):
+        c = W.random_transfer(300 + seed, 2, 300, 4, 1, 8, [37, 0, 90, 5, 211])
+        buf, e1 = o.pack(c.src_caches, c.src_tables)
+        want, e2 = o.unpack([buf], c.dst_caches, c.dst_tables)
+        got, e3 = o.copy_direct(c.src_caches, c.dst_caches, c.src_tables, c.dst_tables)
+        assert e1 == e2 == e3 == 0
+        for l in range(2):
+            assert np.array_equal(got[l], want[l])
+
+
+def pin_direct_out_of_range(o):
+    """An entry with either id out of range moves nothing; every other entry moves."""
+    caches = _tagged_caches(1, 8, 16)
+    before = [np.full((6, 16), 0xEE, np.uint8)]
+    out, err = o.copy_direct(caches, before, [np.array([1, 9, 3]), np.array([-1, 4, 2])],
+                             [np.array([0, 1, 7]), np.array([2, 5, -1])])
+    assert err == o.DEVERR_BLOCK_RANGE
+    got = [None if np.all(out[0][b] == 0xEE) else int(out[0][b][0]) for b in range(6)]
+    assert got == [1, None, None, None, None, 4]
+
+
 def pin_unpack_equals_index_put(o):
     c = W.random_transfer(22, 2, 200, 4, 2, 4, [13, 0, 50, 7])
     buf, _ = o.pack(c.src_caches, c.src_tables)

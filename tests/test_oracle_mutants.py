@@ -34,6 +34,9 @@ MUTANTS = [
     ("pack_dedups_shared_blocks", "            buf[l, p] = caches[l][b]\n    return buf, err",
      "            if any(int(src_tables[rr][jj]) == b for rr, jj, pp in order if pp < p):\n                continue\n"
      "            buf[l, p] = caches[l][b]\n    return buf, err"),
+    ("direct_reads_dst_id", "out[l][d] = srcs[l][s]", "out[l][d] = srcs[l][d % nbs]"),
+    ("direct_layer0_only", "out[l][d] = srcs[l][s]", "out[l][d] = srcs[0][s]"),
+    ("direct_no_dst_range_check", "if s < 0 or s >= nbs or d < 0 or d >= nbd:", "if s < 0 or s >= nbs or d >= nbd:"),
     ("runs_direct_ignores_dst", "                if uses_dst and dst[k] != dst[k - 1] + 1:",
      "                if uses_dst and not uses_src and dst[k] != dst[k - 1] + 1:"),
     ("pack_no_range_check", "if b < 0 or b >= nb:", "if b >= nb:"),
