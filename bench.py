@@ -287,6 +287,19 @@ def main():
                           "median_ms": round(med, 5), "GB/s": round(copy_bytes / (med * 1e-3) / 1e9, 1),
                           "frac_of_peak": round(copy_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                           "traffic": traffic_from_counters(f"{n}_{case.name}", copy_bytes)}
+        # the same transfer with no send buffer: direct-mode runs, cache to cache
+        xd, cd = K.new_xfer_list(N, dev)
+        K.kvx_build_xfer_list(sid, did, ro, K.MODE_DIRECT, xd, cd, err)
+        med, mn = time_op(torch, lambda: K.kvx_copy_direct(src_bases, dst_bases, BB, nb, nb, xd, cd, N, err),
+                          args.op_reps, flush)
+        direct_bytes = copy_bytes  # each listed block read once from the source, written once
+        out_ops["copy_direct"] = {
+            "workload": f"{case.name}: the same 48 layers and tables, cache to cache with no send buffer",
+            "runs": int(cd.item()) * L, "median_ms": round(med, 5),
+            "GB/s": round(direct_bytes / (med * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(direct_bytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "traffic": traffic_from_counters(f"direct_{case.name}", direct_bytes),
+            "vs_pack_plus_unpack": round((out_ops["pack"]["flushed_median_ms"] + out_ops["unpack"]["flushed_median_ms"]) / med, 3)}
         torch.cuda.synchronize()
         assert int(err.item()) == 0, "device error flag raised"
         out_ops["layer_pipeline"] = layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err,

@@ -104,9 +104,9 @@ kvx_status kvx_pack(void* const* layer_bases, int32_t num_layers, int64_t block_
   if (num_layers == 0 || total_blocks == 0) return KVX_SUCCESS;
   if (!layer_bases || !xfers || !xfer_count || !send_buf) return KVX_ERR_INVALID_ARGUMENT;
   if (!mult16(block_bytes) || !aligned16(send_buf)) return KVX_ERR_MISALIGNED;
-  return from_hip(kvx::launch_copy_runs(true, layer_bases, num_layers, block_bytes,
-                                        num_cache_blocks, xfers, xfer_count, total_blocks,
-                                        send_buf, err_flag, stream));
+  return from_hip(kvx::launch_copy_runs(kvx::kDirToBuffer, layer_bases, nullptr, num_layers,
+                                        block_bytes, num_cache_blocks, 0, xfers, xfer_count,
+                                        total_blocks, send_buf, err_flag, stream));
 }
 
 kvx_status kvx_unpack(const void* const* send_bufs, int32_t num_src, void* const* layer_bases,
@@ -128,12 +128,31 @@ kvx_status kvx_unpack(const void* const* send_bufs, int32_t num_src, void* const
     if (!aligned16(send_bufs[s])) return KVX_ERR_MISALIGNED;
   }
   if (num_src == 1)
-    return from_hip(kvx::launch_copy_runs(false, layer_bases, num_layers, block_bytes,
-                                          num_cache_blocks, xfers, xfer_count, total_blocks,
-                                          const_cast<void*>(send_bufs[0]), err_flag, stream));
+    return from_hip(kvx::launch_copy_runs(kvx::kDirFromBuffer, layer_bases, nullptr, num_layers,
+                                          block_bytes, num_cache_blocks, 0, xfers, xfer_count,
+                                          total_blocks, const_cast<void*>(send_bufs[0]), err_flag,
+                                          stream));
   return from_hip(kvx::launch_shards(false, const_cast<void* const*>(send_bufs), num_src, layer_bases,
                                      num_layers, block_bytes, num_cache_blocks, rows_per_block,
                                      xfers, xfer_count, total_blocks, err_flag, stream));
+}
+
+kvx_status kvx_copy_direct(void* const* src_layer_bases, void* const* dst_layer_bases,
+                           int32_t num_layers, int64_t block_bytes, int64_t src_num_blocks,
+                           int64_t dst_num_blocks, const kvx_xfer* xfers,
+                           const int64_t* xfer_count, int64_t total_blocks, int32_t* err_flag,
+                           hipStream_t stream) {
+  if (num_layers < 0 || block_bytes <= 0 || src_num_blocks < 0 || dst_num_blocks < 0 ||
+      total_blocks < 0 || total_blocks > kMaxBlocks)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (num_layers == 0 || total_blocks == 0) return KVX_SUCCESS;
+  if (!src_layer_bases || !dst_layer_bases || !xfers || !xfer_count || src_num_blocks == 0)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (!mult16(block_bytes)) return KVX_ERR_MISALIGNED;
+  return from_hip(kvx::launch_copy_runs(kvx::kDirDirect, src_layer_bases, dst_layer_bases,
+                                        num_layers, block_bytes, src_num_blocks, dst_num_blocks,
+                                        xfers, xfer_count, total_blocks, nullptr, err_flag,
+                                        stream));
 }
 
 kvx_status kvx_pack_split(void* const* layer_bases, int32_t num_layers, int64_t block_bytes,

@@ -42,6 +42,8 @@ const Tuning& tuning() {
        (int)env_i64("KVX_BATCH_SPLIT", 4)},
       {0, (int)env_i64("KVX_NT_KVF_PACK", 3), (int)env_i64("KVX_BATCH_KVF_PACK", 8)},
       {0, (int)env_i64("KVX_NT_KVF_UNPACK", 3), (int)env_i64("KVX_BATCH_KVF_UNPACK", 8)},
+      {env_i64("KVX_WAVE_BYTES_DIRECT", 8 * 1024), (int)env_i64("KVX_NT_DIRECT", 3),
+       (int)env_i64("KVX_BATCH_DIRECT", 8)},
       (int)env_i64("KVX_XCD_REMAP", 1),
       (int)env_i64("KVX_ONE_BATCH", 1),
       (int)env_i64("KVX_NT_WRITE", 1),
@@ -615,14 +617,20 @@ __global__ __launch_bounds__(kScanThreads) void build_xfer_kernel(
 // a4 / a5 — pack and single-source unpack over the run list
 // --------------------------------------------------------------------------------------
 
+// Direction of a run copy: cache -> buffer (pack), buffer -> cache (unpack), or cache ->
+// cache with no buffer (direct: every run's source and destination blocks are consecutive).
+constexpr int kToBuffer = kDirToBuffer, kFromBuffer = kDirFromBuffer, kDirect = kDirDirect;
+
 struct RunCopyArgs {
-  const char* const* layer_bases;
-  char* buffer;
+  const char* const* layer_bases;      // the cache read (pack, direct) or written (unpack)
+  const char* const* dst_layer_bases;  // direct only: the cache written
+  char* buffer;                        // pack and unpack only
   const kvx_xfer* xfers;
   const int64_t* xfer_count;
   int32_t* err;
   int64_t block_bytes;
   int64_t num_cache_blocks;
+  int64_t dst_num_cache_blocks;        // direct only
   int64_t total_blocks;
   int64_t blocks_per_wave;
   int64_t waves_per_layer;
@@ -638,7 +646,7 @@ struct RunCopyArgs {
 // same number of bytes whatever the run lengths. It finds the run holding its first
 // position, then walks the runs overlapping its range; each overlap is one contiguous copy
 // on both sides (run blocks are consecutive in the cache and in the buffer).
-template <bool TO_BUFFER, bool NTL, bool NTS>
+template <int DIR, bool NTL, bool NTS>
 __global__ __launch_bounds__(kCopyThreads) void copy_runs_kernel(RunCopyArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t wg = blockIdx.x;
@@ -655,7 +663,8 @@ __global__ __launch_bounds__(kCopyThreads) void copy_runs_kernel(RunCopyArgs a) 
   if (count > N) count = N;
   if (count <= 0) return;
   char* cache = const_cast<char*>(a.layer_bases[l]);
-  char* buf = a.buffer + l * N * BB;
+  char* dcache = DIR == kDirect ? const_cast<char*>(a.dst_layer_bases[l]) : nullptr;
+  char* buf = DIR == kDirect ? nullptr : a.buffer + l * N * BB;
 
   int64_t k = uniform(find_run(a.xfers, count, p0, lane));
   if (k < 0) k = 0;
@@ -664,20 +673,28 @@ __global__ __launch_bounds__(kCopyThreads) void copy_runs_kernel(RunCopyArgs a) 
     const kvx_xfer x = a.xfers[k];
     const int64_t rb = x.buf_block;
     if (rb >= p1) break;
-    const int64_t lo = rb > p0 ? rb : p0;
+    int64_t lo = rb > p0 ? rb : p0;
     const int64_t re = rb + (int64_t)x.num_blocks;
-    const int64_t hi = re < p1 ? re : p1;
+    int64_t hi = re < p1 ? re : p1;
     if (lo >= hi) continue;
-    const int64_t id0 = (TO_BUFFER ? x.src_block : x.dst_block) + (lo - rb);
-    const int64_t id1 = id0 + (hi - lo);
-    const int64_t v0 = id0 > 0 ? id0 : 0;
-    const int64_t v1 = id1 < a.num_cache_blocks ? id1 : a.num_cache_blocks;
-    if (v0 != id0 || v1 != id1) bad = true;
-    if (v0 >= v1) continue;
-    char* cptr = cache + v0 * BB;
-    char* bptr = buf + (lo + (v0 - id0)) * BB;
-    if (TO_BUFFER) wave_copy<kCopyBatch, NTL, NTS>(cptr, bptr, (v1 - v0) * BB, lane);
-    else wave_copy<kCopyBatch, NTL, NTS>(bptr, cptr, (v1 - v0) * BB, lane);
+    // positions [lo, hi) of the run; trim the ends whose ids fall outside their cache
+    const int64_t sid = (DIR == kFromBuffer ? x.dst_block : x.src_block) + (lo - rb);
+    int64_t nlo = lo, nhi = hi;
+    if (sid < 0) nlo = lo - sid;
+    if (sid + (hi - lo) > a.num_cache_blocks) nhi = lo + (a.num_cache_blocks - sid);
+    int64_t did = 0;
+    if (DIR == kDirect) {
+      did = x.dst_block + (lo - rb);
+      if (lo - did > nlo) nlo = lo - did;
+      if (lo + (a.dst_num_cache_blocks - did) < nhi) nhi = lo + (a.dst_num_cache_blocks - did);
+    }
+    if (nlo != lo || nhi != hi) bad = true;
+    if (nlo >= nhi) continue;
+    const int64_t bytes = (nhi - nlo) * BB;
+    char* cptr = cache + (sid + (nlo - lo)) * BB;
+    if (DIR == kToBuffer) wave_copy<kCopyBatch, NTL, NTS>(cptr, buf + nlo * BB, bytes, lane);
+    else if (DIR == kFromBuffer) wave_copy<kCopyBatch, NTL, NTS>(buf + nlo * BB, cptr, bytes, lane);
+    else wave_copy<kCopyBatch, NTL, NTS>(cptr, dcache + (did + (nlo - lo)) * BB, bytes, lane);
   }
   if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_BLOCK_RANGE);
 }
@@ -803,7 +820,7 @@ __global__ __launch_bounds__(kCopyThreads) void shard_runs_kernel(ShardArgs a) {
 // then the wavefront issues all its loads, then all its stores, and exits. On this
 // architecture stores count in vmcnt, so a wavefront with a second batch would wait for its
 // first batch's store acknowledgements; one batch per wavefront never does.
-template <bool TO_BUFFER, bool NTL, bool NTS, int K>
+template <int DIR, bool NTL, bool NTS, int K>
 __global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(RunCopyArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t wg = blockIdx.x;
@@ -820,7 +837,8 @@ __global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(RunCopyArgs a)
   if (count > N) count = N;
   if (count <= 0) return;
   char* cache = const_cast<char*>(*readonly(a.layer_bases + l));
-  char* buf = a.buffer + l * layer_bytes;
+  char* dcache = DIR == kDirect ? const_cast<char*>(*readonly(a.dst_layer_bases + l)) : nullptr;
+  char* buf = DIR == kDirect ? nullptr : a.buffer + l * layer_bytes;
 
   const int64_t o0 = u * ((int64_t)K * kWaveBytes);
   int64_t q = o0 / BB;       // buffer position of the first slot
@@ -828,9 +846,11 @@ __global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(RunCopyArgs a)
   int64_t k = uniform(find_run(a.xfers, count, q, lane));
   if (k < 0) k = 0;
   Run x = load_run(xf, k);
-  // Slots with nothing to move load from `idle` (1 KiB of this wavefront's own buffer range,
-  // always inside the allocation) so every load is unconditional; only stores are skipped.
-  const char* idle = buf + o0;
+  // Slots with nothing to move load from `idle` so every load is unconditional; only
+  // stores are skipped. It is 1 KiB inside an allocation this launch owns: this wavefront's
+  // own buffer range, or for a direct copy the first KiB of the source layer (whose cache
+  // has at least one block).
+  const char* idle = DIR == kDirect ? cache : buf + o0;
   const char* sp[K];
   char* dp[K];
   bool on[K];
@@ -844,12 +864,15 @@ __global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(RunCopyArgs a)
     if (o < layer_bytes) {
       while (x.buf + x.n <= q && k + 1 < count) x = load_run(xf, ++k);
       if (q >= x.buf && q < x.buf + x.n) {
-        const int64_t id = (TO_BUFFER ? x.src : x.dst) + (q - x.buf);
-        if (id >= 0 && id < a.num_cache_blocks) {
+        const int64_t id = (DIR == kFromBuffer ? x.dst : x.src) + (q - x.buf);
+        const int64_t did = DIR == kDirect ? x.dst + (q - x.buf) : 0;
+        const bool ok = id >= 0 && id < a.num_cache_blocks &&
+                        (DIR != kDirect || (did >= 0 && did < a.dst_num_cache_blocks));
+        if (ok) {
           char* c = cache + id * BB + off;
-          char* b = buf + o;
-          sp[j] = TO_BUFFER ? c : b;
-          dp[j] = TO_BUFFER ? b : c;
+          if (DIR == kToBuffer) { sp[j] = c; dp[j] = buf + o; }
+          else if (DIR == kFromBuffer) { sp[j] = buf + o; dp[j] = c; }
+          else { sp[j] = c; dp[j] = dcache + did * BB + off; }
           on[j] = true;
         } else {
           bad = true;
@@ -1203,20 +1226,24 @@ static bool use_slots(bool whole_kib, int64_t num_layers, int64_t layer_bytes, i
   return ceil_div(waves, kCopyWavesPerWg) < ((int64_t)1 << 31);
 }
 
-hipError_t launch_copy_runs(bool to_buffer, void* const* layer_bases, int32_t num_layers,
-                            int64_t block_bytes, int64_t num_cache_blocks, const kvx_xfer* xfers,
+hipError_t launch_copy_runs(int dir, void* const* layer_bases, void* const* dst_layer_bases,
+                            int32_t num_layers, int64_t block_bytes, int64_t num_cache_blocks,
+                            int64_t dst_num_cache_blocks, const kvx_xfer* xfers,
                             const int64_t* xfer_count, int64_t total_blocks, void* buffer,
                             int32_t* err, hipStream_t stream) {
   RunCopyArgs a;
   a.layer_bases = (const char* const*)layer_bases;
+  a.dst_layer_bases = (const char* const*)dst_layer_bases;
   a.buffer = (char*)buffer;
   a.xfers = xfers;
   a.xfer_count = xfer_count;
   a.err = err;
   a.block_bytes = block_bytes;
   a.num_cache_blocks = num_cache_blocks;
+  a.dst_num_cache_blocks = dst_num_cache_blocks;
   a.total_blocks = total_blocks;
-  const CopyTuning& ct = to_buffer ? tuning().pack : tuning().unpack;
+  const CopyTuning& ct = dir == kToBuffer ? tuning().pack
+                         : dir == kFromBuffer ? tuning().unpack : tuning().direct;
   const int K = batch_of(ct);
   const int64_t unit = (int64_t)K * kWaveBytes;
   const bool slots = use_slots(block_bytes % kWaveBytes == 0, num_layers, total_blocks * block_bytes, unit);
@@ -1232,16 +1259,21 @@ hipError_t launch_copy_runs(bool to_buffer, void* const* layer_bases, int32_t nu
   a.num_layers = num_layers;
   a.xcd_remap = tuning().xcd_remap;
   const unsigned grid = (unsigned)a.num_wgs;
-#define KVX_COPY_T(NTL, NTS, KB)                                                           \
-  if (slots) copy_slots_kernel<true, NTL, NTS, KB><<<grid, kCopyThreads, 0, stream>>>(a); \
-  else copy_runs_kernel<true, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
-#define KVX_COPY_F(NTL, NTS, KB)                                                            \
-  if (slots) copy_slots_kernel<false, NTL, NTS, KB><<<grid, kCopyThreads, 0, stream>>>(a); \
-  else copy_runs_kernel<false, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
-  if (to_buffer) { KVX_POLICY_SWITCH(ct.nt_mode, K, KVX_COPY_T) }
-  else { KVX_POLICY_SWITCH(ct.nt_mode, K, KVX_COPY_F) }
+#define KVX_COPY_T(NTL, NTS, KB)                                                                \
+  if (slots) copy_slots_kernel<kToBuffer, NTL, NTS, KB><<<grid, kCopyThreads, 0, stream>>>(a); \
+  else copy_runs_kernel<kToBuffer, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
+#define KVX_COPY_F(NTL, NTS, KB)                                                                  \
+  if (slots) copy_slots_kernel<kFromBuffer, NTL, NTS, KB><<<grid, kCopyThreads, 0, stream>>>(a); \
+  else copy_runs_kernel<kFromBuffer, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
+#define KVX_COPY_X(NTL, NTS, KB)                                                              \
+  if (slots) copy_slots_kernel<kDirect, NTL, NTS, KB><<<grid, kCopyThreads, 0, stream>>>(a); \
+  else copy_runs_kernel<kDirect, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
+  if (dir == kToBuffer) { KVX_POLICY_SWITCH(ct.nt_mode, K, KVX_COPY_T) }
+  else if (dir == kFromBuffer) { KVX_POLICY_SWITCH(ct.nt_mode, K, KVX_COPY_F) }
+  else { KVX_POLICY_SWITCH(ct.nt_mode, K, KVX_COPY_X) }
 #undef KVX_COPY_T
 #undef KVX_COPY_F
+#undef KVX_COPY_X
   return hipGetLastError();
 }
 

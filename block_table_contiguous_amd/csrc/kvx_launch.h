@@ -14,12 +14,12 @@ namespace kvx {
 // Per copy kernel: bytes of buffer one wavefront owns, the cache policy (bit 0:
 // non-temporal loads, bit 1: non-temporal stores) and the batch of the one-batch kernels.
 struct CopyTuning {
-  int64_t wave_bytes;  // general path (KVX_WAVE_BYTES_{PACK,UNPACK,MERGE,SPLIT})
-  int nt_mode;         // KVX_NT_{PACK,UNPACK,MERGE,SPLIT}
+  int64_t wave_bytes;  // general path (KVX_WAVE_BYTES_{PACK,UNPACK,MERGE,SPLIT,DIRECT})
+  int nt_mode;         // KVX_NT_{PACK,UNPACK,MERGE,SPLIT,DIRECT,KVF_PACK,KVF_UNPACK}
   int batch;           // one-batch path: KiB per wavefront, 4 or 8 (KVX_BATCH_{...})
 };
 struct Tuning {
-  CopyTuning pack, unpack, merge, split, kvf_pack, kvf_unpack;
+  CopyTuning pack, unpack, merge, split, kvf_pack, kvf_unpack, direct;
   int xcd_remap;  // 1: give each XCD a contiguous slice of the work (KVX_XCD_REMAP)
   int one_batch;  // 1: one-batch-per-wavefront kernels where blocks allow (KVX_ONE_BATCH)
   int write_nt;   // cache policy of the new-token write, bits as nt_mode (KVX_NT_WRITE)
@@ -43,9 +43,12 @@ hipError_t launch_build_xfer_list(const int32_t* src_ids, const int32_t* dst_ids
                                   int64_t total_blocks, int32_t mode, kvx_xfer* xfers,
                                   int64_t* xfer_count, int32_t* err, hipStream_t stream);
 
-// pack (to_buffer = true) or single-source unpack (to_buffer = false)
-hipError_t launch_copy_runs(bool to_buffer, void* const* layer_bases, int32_t num_layers,
-                            int64_t block_bytes, int64_t num_cache_blocks, const kvx_xfer* xfers,
+// Run copies: pack (layer_bases -> buffer), single-source unpack (buffer -> layer_bases) or
+// direct (layer_bases -> dst_layer_bases, no buffer).
+enum { kDirToBuffer = 0, kDirFromBuffer = 1, kDirDirect = 2 };
+hipError_t launch_copy_runs(int dir, void* const* layer_bases, void* const* dst_layer_bases,
+                            int32_t num_layers, int64_t block_bytes, int64_t num_cache_blocks,
+                            int64_t dst_num_cache_blocks, const kvx_xfer* xfers,
                             const int64_t* xfer_count, int64_t total_blocks, void* buffer,
                             int32_t* err, hipStream_t stream);
 

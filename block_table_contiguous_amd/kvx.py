@@ -54,6 +54,7 @@ SIGNATURES = {
     "kvx_pack_split": (ctypes.c_int, [_P, _I32, _I64, _I64, _I32, _P, _P, _I64, _P, _I32, _P, _P]),
     "kvx_pack_kv_first": (ctypes.c_int, [_P, _I32, _I64, _I64, _I64, _P, _I32, _P, _P, _I64, _P, _P, _P]),
     "kvx_unpack_kv_first": (ctypes.c_int, [_P, _P, _I32, _I64, _I64, _I64, _P, _I32, _P, _P, _I64, _P, _P]),
+    "kvx_copy_direct": (ctypes.c_int, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _I64, _P, _P]),
     "kvx_signal_add": (ctypes.c_int, [_P, ctypes.c_uint64, _P]),
     "kvx_signal_wait": (ctypes.c_int, [_P, ctypes.c_uint64, _I64, _P, _P]),
 }
@@ -297,6 +298,25 @@ def kvx_unpack(send_bufs: Sequence, layer_bases, block_bytes: int, num_cache_blo
                           int(rows_per_block), _ptr(xfers), _ptr(xfer_count), int(total_blocks),
                           _ptr(err_flag), _stream(stream))
     _check("kvx_unpack", st)
+
+
+def kvx_copy_direct(src_layer_bases, dst_layer_bases, block_bytes: int, src_num_blocks: int,
+                    dst_num_blocks: int, xfers, xfer_count, total_blocks: int, err_flag=None,
+                    stream=None):
+    """Copy the listed blocks of every layer from the source caches straight into the
+    destination caches (no buffer); the runs come from kvx_build_xfer_list(MODE_DIRECT)."""
+    import torch
+
+    _want(src_layer_bases, torch.int64, "src_layer_bases")
+    _want(dst_layer_bases, torch.int64, "dst_layer_bases")
+    _want_runs(xfers, xfer_count, total_blocks)
+    L = src_layer_bases.numel()
+    if dst_layer_bases.numel() != L:
+        raise ValueError("kvx: source and destination layer tables differ in length")
+    st = _F["kvx_copy_direct"](_ptr(src_layer_bases), _ptr(dst_layer_bases), L, int(block_bytes),
+                               int(src_num_blocks), int(dst_num_blocks), _ptr(xfers), _ptr(xfer_count),
+                               int(total_blocks), _ptr(err_flag), _stream(stream))
+    _check("kvx_copy_direct", st)
 
 
 def kvx_pack_split(layer_bases, block_bytes: int, num_cache_blocks: int, rows_per_block: int,

@@ -216,6 +216,29 @@ kvx_status kvx_unpack(const void* const* send_bufs, int32_t num_src, void* const
                       hipStream_t stream);
 
 /*
+ * kvx_copy_direct — move the listed blocks of every layer straight from the sender's caches
+ * into the receiver's, with no send buffer ("vLLM PD 分离" §四 4.2: one write per source
+ * address, destination address and length, from the prefill cache into the decode cache;
+ * §七 item 3: address = layer base + block length x id). For layer l and every run, blocks
+ * src_block .. src_block + num_blocks - 1 of src layer l go to dst_block .. of dst layer l.
+ * It is the one-pass form of pack + unpack: 2 x block_bytes of HBM traffic per (layer, block)
+ * instead of 4, and the data-parallel part of a one-sided transfer whose destination is a
+ * peer's cache.
+ *   src_layer_bases / dst_layer_bases  device arrays [num_layers] of layer base pointers.
+ *   src_num_blocks / dst_num_blocks    blocks per layer on each side (src_num_blocks >= 1).
+ *   xfers, xfer_count, total_blocks    a run list built with KVX_MODE_DIRECT (runs
+ *                                      consecutive on both sides).
+ * An entry whose source or destination id is outside its cache is skipped and raises
+ * KVX_DEVERR_BLOCK_RANGE. Errors: INVALID_ARGUMENT for NULL pointers (when there is work),
+ * negative sizes or src_num_blocks == 0; MISALIGNED for block_bytes not a multiple of 16.
+ */
+kvx_status kvx_copy_direct(void* const* src_layer_bases, void* const* dst_layer_bases,
+                           int32_t num_layers, int64_t block_bytes, int64_t src_num_blocks,
+                           int64_t dst_num_blocks, const kvx_xfer* xfers,
+                           const int64_t* xfer_count, int64_t total_blocks, int32_t* err_flag,
+                           hipStream_t stream);
+
+/*
  * kvx_pack_split — sender-side head split for an asymmetric TP transfer where the receiver
  * runs num_dst ranks ("vLLM PD 分离" §四 4.2, TP heterogeneity): the inverse of kvx_unpack's
  * merge. Every full-head cache block is rows_per_block rows (block_size*2 for the

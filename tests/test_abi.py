@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "kvx_abi_version", "kvx_build_xfer_list", "kvx_pack", "kvx_reshape_and_cache",
         "kvx_slot_mapping", "kvx_status_string", "kvx_unpack", "kvx_pack_split",
-        "kvx_pack_kv_first", "kvx_unpack_kv_first", "kvx_signal_add", "kvx_signal_wait"])
+        "kvx_pack_kv_first", "kvx_unpack_kv_first", "kvx_signal_add", "kvx_signal_wait",
+        "kvx_copy_direct"])
 
 
 def test_every_declared_symbol_is_exported(kvx):
@@ -187,3 +188,18 @@ def test_binding_rejects_undersized_tensors(kvx):
         kvx.kvx_unpack([buf, buf[:100]], bases, 64, 100, 2, x10, c, 10)
     with pytest.raises(TypeError):
         kvx.kvx_pack(bases, 64, 100, x10.int(), c, 10, buf)
+
+
+def test_copy_direct_validation(kvx):
+    def direct(sb=P, db=P, L=2, bb=8192, nbs=100, nbd=100, x=P, cnt=P, n=10):
+        return call(kvx, "kvx_copy_direct", sb, db, L, bb, nbs, nbd, x, cnt, n, None, None)
+    assert direct(L=-1) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert direct(bb=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert direct(nbd=-1) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert direct(n=1 << 31) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert direct(sb=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert direct(db=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert direct(x=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert direct(nbs=0) == kvx.KVX_ERR_INVALID_ARGUMENT  # nothing to read from
+    assert direct(bb=8200) == kvx.KVX_ERR_MISALIGNED
+    assert direct(n=0, sb=None) == kvx.KVX_SUCCESS

@@ -221,3 +221,38 @@ def test_layer_pipelined_transfer_full(pages_caches):
     assert int(werr.item()) == 0 and int(counter.item()) == L
     log("layer-pipelined transfer done, checking")
     _verify(case, tr)
+
+
+def test_pages_contiguous_direct_full(pages_caches):
+    """The contiguous transfer at full size with no send buffer: runs built in direct mode,
+    every listed block of the 48 layers copied from the source caches into the destination
+    caches. Three layers checked in full against the oracle, all layers on sampled blocks."""
+    spec, src, dst = pages_caches
+    case = W.pages_contiguous()
+    K = kvx()
+    L, nb, BB, N = spec.num_layers, spec.num_blocks, spec.block_bytes, case.total_blocks
+    for t in dst:
+        W.fill_device_byte_(t)
+    sid, ro = K.flatten_tables(case.src_tables, DEV)
+    did, _ = K.flatten_tables(case.dst_tables, DEV)
+    x, c = K.new_xfer_list(N, DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    K.kvx_build_xfer_list(sid, did, ro, K.MODE_DIRECT, x, c, err)
+    K.kvx_copy_direct(K.layer_base_table(src), K.layer_base_table(dst), BB, nb, nb, x, c, N, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    check_runs_equal(K, x, c, O.xfer_list(case.src_tables, case.dst_tables, O.MODE_DIRECT))
+    for l in FULL_LAYERS:
+        before = np.full((nb, BB), W.FILL_BYTE, np.uint8)
+        exp, e = O.copy_direct([host_bytes(src[l]).reshape(nb, BB)], [before], case.src_tables,
+                               case.dst_tables)
+        assert e == 0
+        assert np.array_equal(host_bytes(dst[l]).reshape(nb, BB), exp[0]), f"direct layer {l}"
+        log(f"direct: layer {l} identical")
+    rng = np.random.default_rng(case.seed + 1)
+    flat_s, flat_d = np.concatenate(case.src_tables), np.concatenate(case.dst_tables)
+    for _ in range(SAMPLES):
+        l = int(rng.integers(L))
+        i = int(rng.integers(N))
+        assert np.array_equal(host_bytes(dst[l][int(flat_d[i])]), host_bytes(src[l][int(flat_s[i])])), (l, i)
+    log(f"direct: {SAMPLES} sampled blocks identical")
