@@ -167,3 +167,43 @@ def test_layer_pipelined_transfer_whole_kib_blocks():
     rng = np.random.default_rng(32)
     lengths = [int(x) for x in rng.integers(100, 1500, size=5)]
     _pipelined_roundtrip(32, 8, 800, 1, 128, lengths, 2)
+
+
+def test_layer_pipelined_direct_copy_then_consumer_reads():
+    """Per layer: the producer copies the layer's blocks cache to cache (no buffer) and adds 1;
+    the consumer waits for that count, then copies the destination layer out with a kernel
+    of its own (a torch copy). What the consumer read must be the oracle's direct copy: the
+    wait ordered its reads after the producer's writes."""
+    K = kvx()
+    rng = np.random.default_rng(33)
+    lengths = [int(x) for x in rng.integers(100, 1200, size=5)]
+    L, nb = 6, 700
+    case = W.random_transfer(33, L, nb, 16, 1, 128, lengths)
+    BB, N = case.src_spec.block_bytes, case.total_blocks
+    src = layers_from_host(case.src_caches, BB)
+    dst = layers_from_host(case.dst_caches, BB)
+    seen = [torch.empty_like(t) for t in dst]
+    sb, db = K.layer_base_table(src), K.layer_base_table(dst)
+    sid, ro = K.flatten_tables(case.src_tables, DEV)
+    did, _ = K.flatten_tables(case.dst_tables, DEV)
+    x, c = K.new_xfer_list(N, DEV)
+    counter = torch.zeros(1, dtype=torch.int64, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    werr = torch.zeros(1, dtype=torch.int32, device=DEV)
+    K.kvx_build_xfer_list(sid, did, ro, K.MODE_DIRECT, x, c, err)
+    torch.cuda.synchronize()
+    prod, cons = torch.cuda.Stream(), torch.cuda.Stream()
+    for l in range(L):
+        with torch.cuda.stream(prod):
+            _busy(2, 2048)
+            K.kvx_copy_direct(sb[l:l + 1], db[l:l + 1], BB, nb, nb, x, c, N, err)
+            K.kvx_signal_add(counter, 1)
+        with torch.cuda.stream(cons):
+            K.kvx_signal_wait(counter, l + 1, 20_000_000, werr)
+            seen[l].copy_(dst[l])
+    torch.cuda.synchronize()
+    assert int(werr.item()) == 0 and int(err.item()) == 0 and int(counter.item()) == L
+    exp, e = O.copy_direct(case.src_caches, case.dst_caches, case.src_tables, case.dst_tables)
+    assert e == 0
+    for l in range(L):
+        assert np.array_equal(host_bytes(seen[l]).reshape(nb, BB), exp[l]), f"layer {l}"
