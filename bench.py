@@ -12,11 +12,16 @@ One step = one pass of the whole hot path over that batch:
             -> kvx_slot_mapping for each request's recomputed last prompt token
             -> kvx_reshape_and_cache of those 8 tokens into each of the 48 layers
 `value` = algorithmic bytes of the step (read + write of every moved byte) / step time.
-The asymmetric-TP head merge and the 32-request decode write run on their own workloads in
-the same process and are reported under "ops", each with its own roofline.
+"roofline" is the slower of pack and unpack in the timed steps (HIP events on their stream).
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ops]
-Prints one JSON line on stdout.
+Under "ops", each after evicting the Infinity Cache: the same caches as kv-first views, the
+direct cache-to-cache copy, the layer-pipelined pack beside a GEMM forward stand-in, the
+asymmetric-TP head merge and split (32 layers, 64 KiB blocks), and the 32-request decode
+slot mapping and new-token write. "cpu_baseline" is the CPU oracle on the whole step.
+
+    python bench.py [--steps K] [--warmup W] [--workload contiguous|fragmented]
+                    [--no-cpu-baseline] [--no-ops] [--graph] [--copy-calib]
+Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
