@@ -228,6 +228,9 @@ kvx_status kvx_unpack(const void* const* send_bufs, int32_t num_src, void* const
  *   src_num_blocks / dst_num_blocks    blocks per layer on each side (src_num_blocks >= 1).
  *   xfers, xfer_count, total_blocks    a run list built with KVX_MODE_DIRECT (runs
  *                                      consecutive on both sides).
+ * The two sides may be the same caches (a copy between blocks of one cache), but no
+ * destination block may also be a source block of the same call, and destination ids must
+ * be unique: blocks move concurrently, in no particular order.
  * An entry whose source or destination id is outside its cache is skipped and raises
  * KVX_DEVERR_BLOCK_RANGE. Errors: INVALID_ARGUMENT for NULL pointers (when there is work),
  * negative sizes or src_num_blocks == 0; MISALIGNED for block_bytes not a multiple of 16.
