@@ -102,3 +102,29 @@ def test_direct_shared_prefix_and_out_of_range():
     src = [W.random_words(rng, (nb, bb // 2)) for _ in range(L)]
     dst = [np.full((nb, bb // 2), W.SENTINEL16, np.uint16) for _ in range(L)]
     assert _direct_case(src_tables, dst_tables, src, dst, bb) == O.DEVERR_BLOCK_RANGE
+
+
+def test_direct_within_one_cache():
+    """Source and destination are the same caches (a copy between blocks of one cache, as when
+    a shared prefix is forked), with disjoint source and destination blocks."""
+    K = kvx()
+    rng = np.random.default_rng(14)
+    L, bb, nb = 2, 4096, 800
+    ids = rng.permutation(nb).astype(np.int32)
+    src_ids, dst_ids = ids[:250], ids[250:500]
+    src_tables = [src_ids[:100], src_ids[100:100], src_ids[100:250]]
+    dst_tables = [dst_ids[:100], dst_ids[100:100], dst_ids[100:250]]
+    caches_h = [W.random_words(rng, (nb, bb // 2)) for _ in range(L)]
+    caches = layers_from_host(caches_h, bb)
+    bases = K.layer_base_table(caches)
+    sid, ro = K.flatten_tables(src_tables, DEV)
+    did, _ = K.flatten_tables(dst_tables, DEV)
+    x, c = K.new_xfer_list(250, DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    K.kvx_build_xfer_list(sid, did, ro, K.MODE_DIRECT, x, c, err)
+    K.kvx_copy_direct(bases, bases, bb, nb, nb, x, c, 250, err)
+    torch.cuda.synchronize()
+    exp, e = O.copy_direct(caches_h, caches_h, src_tables, dst_tables)
+    assert e == 0 and int(err.item()) == 0
+    for l in range(L):
+        assert np.array_equal(host_bytes(caches[l]).reshape(nb, bb), exp[l]), f"layer {l}"
