@@ -376,7 +376,7 @@ __global__ __launch_bounds__(256) void write_slots_kernel(WriteArgs a) {
 }
 
 // --------------------------------------------------------------------------------------
-// a3 — transfer list: run-start flags -> prefix scan -> compaction, one tile per workgroup
+// a3 — transfer list: run-start flags -> prefix scan -> compaction, tiles over up to 256 workgroups
 // --------------------------------------------------------------------------------------
 
 constexpr int kScanThreads = 256;
@@ -388,6 +388,10 @@ constexpr int kScanWaves = kScanThreads / kWave;
 #endif
 constexpr int kPrefixGroups = KVX_PREFIX_GROUPS;       // 1024-position groups per prefix round
 constexpr int kLdsOffsets = 4096;  // request offsets staged in LDS when num_reqs < this
+#ifndef KVX_BUILD_MAX_WGS
+#define KVX_BUILD_MAX_WGS 256
+#endif
+constexpr int64_t kBuildMaxWgs = KVX_BUILD_MAX_WGS;  // one per CU
 
 // Largest r in [0, R) with ro[r] <= p (0 if none).
 template <class P>
@@ -443,32 +447,34 @@ __device__ __forceinline__ void chunk_flags(P ro, int32_t R, int64_t N, bool use
   }
 }
 
-// Workgroup b owns positions [b * kScanTile, (b + 1) * kScanTile). It first counts the run
-// starts before its tile and finds the latest of them (a pass over every earlier id and over
-// the request offsets, no writes), then flags its own positions (8 per
-// thread), turns them into run indices and latest-start positions with a wave scan plus a
-// 4-entry LDS pass, and writes the runs each thread starts and the lengths of the runs it
-// ends. No thread reads another's output, and no workgroup waits for another. Request
-// offsets are staged in LDS when there are fewer than kLdsOffsets requests.
+// Workgroup b owns positions [b * span, (b + 1) * span), span a multiple of kScanTile. It
+// first counts the run starts before its range and finds the latest of them (a pass over
+// every earlier id and over the request offsets, no writes). Then, one kScanTile sub-tile
+// at a time, it flags its positions (8 per thread), turns them into run indices and
+// latest-start positions with a wave scan plus a 4-entry LDS pass, and writes the runs each
+// thread starts and the lengths of the runs it ends, carrying the count and the latest start
+// to the next sub-tile. No thread reads another's output, and no workgroup waits for another.
+// Request offsets are staged in LDS when there are fewer than kLdsOffsets requests.
 template <class P>
 __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
                                            const int32_t* __restrict__ dst, P ro, int32_t R,
                                            int64_t N, bool use_src, bool use_dst,
                                            kvx_xfer* __restrict__ out, int64_t* __restrict__ count,
-                                           int64_t* s_cnt, int64_t* s_last) {
+                                           int64_t span, int64_t* s_cnt, int64_t* s_last) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;
-  const int64_t tile = (int64_t)blockIdx.x * kScanTile;
+  const int64_t begin = (int64_t)blockIdx.x * span;
+  const int64_t end = begin + span < N ? begin + span : N;
 
-  // 1. run starts before the tile: count and latest position. With a valid CSR a position
-  //    p in [1, tile) starts a run iff its ids break the +1 step from p - 1 or a request
+  // 1. run starts before the range: count and latest position. With a valid CSR a position
+  //    p in [1, begin) starts a run iff its ids break the +1 step from p - 1 or a request
   //    starts at p, so the count is: position 0, plus the id breaks, plus the request starts
   //    that are not id breaks. (a) streams the ids in rounds of kPrefixGroups groups of
   //    kScanThreads * 4 positions, 4 consecutive positions per lane; (b) walks the offsets.
   int64_t pc = 0, pl = -1;
-  if (tile > 0) {
-    for (int64_t base = 0; base < tile; base += (int64_t)kScanThreads * 4 * kPrefixGroups) {
+  if (begin > 0) {
+    for (int64_t base = 0; base < begin; base += (int64_t)kScanThreads * 4 * kPrefixGroups) {
       int32_t sv[kPrefixGroups][6], dv[kPrefixGroups][6];
 #pragma unroll
       for (int g = 0; g < kPrefixGroups; ++g)
@@ -476,19 +482,19 @@ __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
                      sv[g], dv[g]);
 #pragma unroll
       for (int g = 0; g < kPrefixGroups; ++g) {
-        const int64_t q0 = base + ((int64_t)g * kScanThreads + tid) * 4;  // never straddles the tile
+        const int64_t q0 = base + ((int64_t)g * kScanThreads + tid) * 4;  // never straddles the range
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t p = q0 + i;
           const bool brk = (use_src && (int64_t)sv[g][i + 1] != (int64_t)sv[g][i] + 1) ||
                            (use_dst && (int64_t)dv[g][i + 1] != (int64_t)dv[g][i] + 1);
-          if (p >= 1 && p < tile && brk) { ++pc; pl = p; }
+          if (p >= 1 && p < begin && brk) { ++pc; pl = p; }
         }
       }
     }
     for (int32_t r = 1 + tid; r < R; r += kScanThreads) {
       const int64_t q = ro[r];
-      if (q >= 1 && q < tile && q != ro[r - 1]) {  // the first request starting at q
+      if (q >= 1 && q < begin && q != ro[r - 1]) {  // the first request starting at q
         pl = q > pl ? q : pl;
         const bool brk = (use_src && (int64_t)src[q] != (int64_t)src[q - 1] + 1) ||
                          (use_dst && (int64_t)dst[q] != (int64_t)dst[q - 1] + 1);
@@ -516,78 +522,84 @@ __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
   }
   __syncthreads();
 
-  // 2. the own tile
-  const int64_t p0 = tile + (int64_t)tid * kScanItems;
-  bool st[kScanItems + 1];
-  int32_t rq[kScanItems], sv[kScanItems + 2], dv[kScanItems + 2];
-  if (N > 0) chunk_ids<kScanItems>(src, dst, N, use_src, use_dst, p0, sv, dv);
-  chunk_flags<kScanItems>(ro, R, N, use_src, use_dst, p0, sv, dv, st, rq);
-  int64_t cnt = 0, last = -1;
+  // 2. the own range, one sub-tile at a time
+  for (int64_t tile = begin; tile < end; tile += kScanTile) {
+    const int64_t p0 = tile + (int64_t)tid * kScanItems;
+    bool st[kScanItems + 1];
+    int32_t rq[kScanItems], sv[kScanItems + 2], dv[kScanItems + 2];
+    if (N > 0) chunk_ids<kScanItems>(src, dst, N, use_src, use_dst, p0, sv, dv);
+    chunk_flags<kScanItems>(ro, R, N, use_src, use_dst, p0, sv, dv, st, rq);
+    int64_t cnt = 0, last = -1;
 #pragma unroll
-  for (int i = 0; i < kScanItems; ++i)
-    if (st[i]) { ++cnt; last = p0 + i; }
+    for (int i = 0; i < kScanItems; ++i)
+      if (st[i]) { ++cnt; last = p0 + i; }
 
-  // workgroup scan of (cnt: sum, last: max)
-  int64_t ci = cnt, li = last;
+    // workgroup scan of (cnt: sum, last: max)
+    int64_t ci = cnt, li = last;
 #pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int64_t c = __shfl_up(ci, d, kWave);
-    const int64_t l = __shfl_up(li, d, kWave);
-    if (lane >= d) { ci += c; li = l > li ? l : li; }
-  }
-  int64_t li_excl = __shfl_up(li, 1, kWave);
-  if (lane == 0) li_excl = -1;
-  if (lane == kWave - 1) { s_cnt[wid] = ci; s_last[wid] = li; }
-  __syncthreads();
-  int64_t c_before = 0, l_before = -1, c_tile = 0;
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int64_t c = __shfl_up(ci, d, kWave);
+      const int64_t l = __shfl_up(li, d, kWave);
+      if (lane >= d) { ci += c; li = l > li ? l : li; }
+    }
+    int64_t li_excl = __shfl_up(li, 1, kWave);
+    if (lane == 0) li_excl = -1;
+    if (lane == kWave - 1) { s_cnt[wid] = ci; s_last[wid] = li; }
+    __syncthreads();
+    int64_t c_before = 0, l_before = -1, c_tile = 0, l_tile = -1;
 #pragma unroll
-  for (int w = 0; w < kScanWaves; ++w) {
-    const int64_t c = s_cnt[w], l = s_last[w];
-    if (w < wid) { c_before += c; l_before = l > l_before ? l : l_before; }
-    c_tile += c;
-  }
+    for (int w = 0; w < kScanWaves; ++w) {
+      const int64_t c = s_cnt[w], l = s_last[w];
+      if (w < wid) { c_before += c; l_before = l > l_before ? l : l_before; }
+      c_tile += c;
+      l_tile = l > l_tile ? l : l_tile;
+    }
 
-  int64_t k = carry_cnt + c_before + (ci - cnt);
-  int64_t cur = carry_last;
-  if (l_before > cur) cur = l_before;
-  if (li_excl > cur) cur = li_excl;
+    int64_t k = carry_cnt + c_before + (ci - cnt);
+    int64_t cur = carry_last;
+    if (l_before > cur) cur = l_before;
+    if (li_excl > cur) cur = li_excl;
 #pragma unroll
-  for (int i = 0; i < kScanItems; ++i) {
-    const int64_t p = p0 + i;
-    if (p < N) {
-      const bool ends = p == N - 1 || st[i + 1];
-      if (k >= N) break;  // only with offsets that are not a CSR (flagged by workgroup 0)
-      if (st[i]) {
-        // a run that starts here: 16-byte stores of (src, dst) and, when it also ends here,
-        // of (buf, num_blocks = 1 | req << 32); the xfer array is 16-byte aligned
-        KVX_GLOBAL i64x2* x = (KVX_GLOBAL i64x2*)(out + k);
-        i64x2 head;
-        head.x = use_src ? (int64_t)sv[i + 1] : p;
-        head.y = use_dst ? (int64_t)dv[i + 1] : p;
-        x[0] = head;
-        if (ends) {
-          i64x2 tail;
-          tail.x = p;
-          tail.y = (int64_t)(((uint64_t)(uint32_t)rq[i] << 32) | 1u);
-          x[1] = tail;
-        } else {
-          out[k].buf_block = p;
-          out[k].req = rq[i];
+    for (int i = 0; i < kScanItems; ++i) {
+      const int64_t p = p0 + i;
+      if (p < N) {
+        const bool ends = p == N - 1 || st[i + 1];
+        if (k >= N) break;  // only with offsets that are not a CSR (flagged by workgroup 0)
+        if (st[i]) {
+          // a run that starts here: 16-byte stores of (src, dst) and, when it also ends here,
+          // of (buf, num_blocks = 1 | req << 32); the xfer array is 16-byte aligned
+          KVX_GLOBAL i64x2* x = (KVX_GLOBAL i64x2*)(out + k);
+          i64x2 head;
+          head.x = use_src ? (int64_t)sv[i + 1] : p;
+          head.y = use_dst ? (int64_t)dv[i + 1] : p;
+          x[0] = head;
+          if (ends) {
+            i64x2 tail;
+            tail.x = p;
+            tail.y = (int64_t)(((uint64_t)(uint32_t)rq[i] << 32) | 1u);
+            x[1] = tail;
+          } else {
+            out[k].buf_block = p;
+            out[k].req = rq[i];
+          }
+          cur = p;
+          ++k;
+        } else if (ends) {
+          out[k - 1].num_blocks = (int32_t)(p - cur + 1);
         }
-        cur = p;
-        ++k;
-      } else if (ends) {
-        out[k - 1].num_blocks = (int32_t)(p - cur + 1);
       }
     }
+    carry_cnt += c_tile;
+    if (l_tile > carry_last) carry_last = l_tile;
+    __syncthreads();  // the next sub-tile reuses s_cnt / s_last
   }
-  if (blockIdx.x == gridDim.x - 1 && tid == 0) *count = carry_cnt + c_tile;
+  if (blockIdx.x == gridDim.x - 1 && tid == 0) *count = carry_cnt;
 }
 
 __global__ __launch_bounds__(kScanThreads) void build_xfer_kernel(
     const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
     const int64_t* __restrict__ ro, int32_t R, int64_t N, int32_t mode,
-    kvx_xfer* __restrict__ out, int64_t* __restrict__ count, int32_t* err) {
+    kvx_xfer* __restrict__ out, int64_t* __restrict__ count, int32_t* err, int64_t span) {
   __shared__ int64_t s_cnt[kScanWaves];
   __shared__ int64_t s_last[kScanWaves];
   __shared__ int64_t s_ro[kLdsOffsets + 1];
@@ -608,9 +620,9 @@ __global__ __launch_bounds__(kScanThreads) void build_xfer_kernel(
   if (check && tid == 0 && (ro[0] != 0 || ro[R] != N)) raise_error(err, KVX_DEVERR_OFFSETS);
   __syncthreads();
   if (in_lds)
-    build_tile<const int64_t*>(src, dst, s_ro, R, N, use_src, use_dst, out, count, s_cnt, s_last);
+    build_tile<const int64_t*>(src, dst, s_ro, R, N, use_src, use_dst, out, count, span, s_cnt, s_last);
   else
-    build_tile<const int64_t*>(src, dst, ro, R, N, use_src, use_dst, out, count, s_cnt, s_last);
+    build_tile<const int64_t*>(src, dst, ro, R, N, use_src, use_dst, out, count, span, s_cnt, s_last);
 }
 
 // --------------------------------------------------------------------------------------
@@ -1183,9 +1195,15 @@ hipError_t launch_build_xfer_list(const int32_t* src_ids, const int32_t* dst_ids
                                   const int64_t* req_offsets, int32_t num_reqs,
                                   int64_t total_blocks, int32_t mode, kvx_xfer* xfers,
                                   int64_t* xfer_count, int32_t* err, hipStream_t stream) {
+  // One workgroup per kScanTile positions up to kBuildMaxWgs workgroups; past that each
+  // workgroup takes several sub-tiles, which keeps the prefix passes' total work within
+  // kBuildMaxWgs / 2 reads per position.
   const int64_t tiles = total_blocks > 0 ? ceil_div(total_blocks, kScanTile) : 1;
-  build_xfer_kernel<<<(unsigned)tiles, kScanThreads, 0, stream>>>(
-      src_ids, dst_ids, req_offsets, num_reqs, total_blocks, mode, xfers, xfer_count, err);
+  const int64_t wgs = tiles < kBuildMaxWgs ? tiles : kBuildMaxWgs;
+  const int64_t span = ceil_div(tiles, wgs) * kScanTile;
+  const int64_t grid = total_blocks > 0 ? ceil_div(total_blocks, span) : 1;
+  build_xfer_kernel<<<(unsigned)grid, kScanThreads, 0, stream>>>(
+      src_ids, dst_ids, req_offsets, num_reqs, total_blocks, mode, xfers, xfer_count, err, span);
   return hipGetLastError();
 }
 

@@ -256,3 +256,29 @@ def test_pages_contiguous_direct_full(pages_caches):
         i = int(rng.integers(N))
         assert np.array_equal(host_bytes(dst[l][int(flat_d[i])]), host_bytes(src[l][int(flat_s[i])])), (l, i)
     log(f"direct: {SAMPLES} sampled blocks identical")
+
+
+def test_run_lists_past_the_workgroup_cap():
+    """1.18M blocks of 16 bytes in 300 requests: more tiles than the run builder's workgroups,
+    so each workgroup walks several sub-tiles. Run lists in both modes and the transfer's
+    bytes against the oracle."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rng = np.random.default_rng(90)
+    lengths = [int(x) for x in rng.integers(0, 8000, size=300)]
+    case = W.random_transfer(91, 1, 3_000_000, 1, 1, 8, lengths, elem_bytes=1)
+    BB = case.src_spec.block_bytes
+    assert case.total_blocks > 256 * 2048
+    src = [torch.from_numpy(case.src_caches[0].view(np.uint8).reshape(-1, BB)).to(DEV)]
+    dst = [torch.from_numpy(case.dst_caches[0].view(np.uint8).reshape(-1, BB)).to(DEV)]
+    tr = Transfer(case, src, dst)
+    tr.run()
+    log("1.18M-block transfer done, checking")
+    assert tr.err_bits() == 0
+    check_runs_equal(tr.K, tr.xp, tr.cp, O.xfer_list(case.src_tables, case.dst_tables, O.MODE_PACK))
+    check_runs_equal(tr.K, tr.xu, tr.cu, O.xfer_list(case.src_tables, case.dst_tables, O.MODE_UNPACK))
+    exp_buf, e1 = O.pack(case.src_caches, case.src_tables)
+    exp_dst, e2 = O.unpack([exp_buf], case.dst_caches, case.dst_tables)
+    assert e1 == e2 == 0
+    assert np.array_equal(host_bytes(tr.buf)[: exp_buf.nbytes], exp_buf.reshape(-1))
+    assert np.array_equal(host_bytes(dst[0]), exp_dst[0].reshape(-1))
