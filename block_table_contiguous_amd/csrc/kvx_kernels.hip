@@ -39,7 +39,7 @@ const Tuning& tuning() {
       {env_i64("KVX_WAVE_BYTES_MERGE", 64 * 1024), (int)env_i64("KVX_NT_MERGE", 3),
        (int)env_i64("KVX_BATCH_MERGE", 8)},
       {env_i64("KVX_WAVE_BYTES_SPLIT", 64 * 1024), (int)env_i64("KVX_NT_SPLIT", 3),
-       (int)env_i64("KVX_BATCH_SPLIT", 4)},
+       (int)env_i64("KVX_BATCH_SPLIT", 8)},
       {0, (int)env_i64("KVX_NT_KVF_PACK", 3), (int)env_i64("KVX_BATCH_KVF_PACK", 8)},
       {0, (int)env_i64("KVX_NT_KVF_UNPACK", 3), (int)env_i64("KVX_BATCH_KVF_UNPACK", 8)},
       {env_i64("KVX_WAVE_BYTES_DIRECT", 8 * 1024), (int)env_i64("KVX_NT_DIRECT", 3),
