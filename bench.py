@@ -18,9 +18,11 @@ Under "ops", each after evicting the Infinity Cache: the same caches as kv-first
 direct cache-to-cache copy, the layer-pipelined pack beside a GEMM forward stand-in, the
 asymmetric-TP head merge and split (32 layers, 64 KiB blocks), and the 32-request decode
 slot mapping and new-token write. "cpu_baseline" is the CPU oracle on the whole step.
+"graph_ms_per_step" is the same step captured once in a HIP graph and replayed (`value`
+stays the eager rate: a graph is fixed to one transfer size).
 
     python bench.py [--steps K] [--warmup W] [--workload contiguous|fragmented]
-                    [--no-cpu-baseline] [--no-ops] [--graph] [--copy-calib]
+                    [--no-cpu-baseline] [--no-ops] [--no-graph] [--copy-calib]
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -63,8 +65,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ops", action="store_true")
     ap.add_argument("--op-reps", type=int, default=10)
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the step replayed from a captured HIP graph (reported as graph_ms_per_step)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the step replayed from a captured HIP graph (graph_ms_per_step)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -218,7 +220,7 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step")
 
     graph_ms = None
-    if args.graph:
+    if not args.no_graph:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -280,6 +282,7 @@ def main():
                       ("unpack", lambda: K.kvx_unpack([buf], dst_bases, BB, nb, 1, xu, cu, N, err))):
             med, mn = time_op(torch, fn, args.op_reps, flush)
             out_ops[n]["flushed_median_ms"] = round(med, 5)
+            out_ops[n]["flushed_min_ms"] = round(mn, 5)
             out_ops[n]["flushed_GB/s"] = round(copy_bytes / (med * 1e-3) / 1e9, 1)
         # the same 48 allocations viewed as kv-first caches: (K plane, V plane) of 4 KiB segments
         seg = BB // 2
@@ -349,17 +352,19 @@ def main():
 def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, reps):
     """The sender's side of a layer-pipelined transfer. One bf16 [8192 x 4096] x [4096 x 4096]
     product per layer on the forward stream stands in for that layer's forward pass (it is not
-    part of the path). Schedules, each timed from a start event to the end of all streams, with
-    the tail (end of the last product to the end of the packing) beside it:
+    part of the path). Schedules, each timed from a start event to the end of all streams:
       forward_only  the 48 products;
       serial        the 48 products, then one pack of all layers on the forward stream;
+      inline        per layer on the forward stream: the product, the pack of that layer into
+                    its slice of the send buffer, and a signal add (the count a transport, or a
+                    receiver's signal wait, follows layer by layer);
       pipelined     per layer: the product, then an event on the forward stream; on a copy
-                    stream, a wait for that event, the pack of that layer into its slice of the
-                    send buffer and a signal add — the count a transport (or a receiver's
-                    signal wait) follows layer by layer. The forward stream never waits for a
-                    copy.
-    The receiver's unpack is left out here: it runs on the other GPU of a real transfer, not
-    beside the sender's forward pass."""
+                    stream, a wait for that event, the layer's pack and the signal add. The
+                    forward stream never waits for a copy.
+    Per schedule: the total, the tail (end of the last product to the end of the packing) and
+    mean_ready (start to the moment a layer's packed bytes are complete, averaged over the
+    layers: when a transport could begin sending each layer). The receiver's unpack is left
+    out: it runs on the other GPU of a real transfer, not beside the sender's forward pass."""
     m, k = 8192, 4096
     a = torch.full((m, k), 0.5, dtype=torch.bfloat16, device=dev)
     b = torch.full((k, k), 0.25, dtype=torch.bfloat16, device=dev)
@@ -370,20 +375,30 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
     evs = [torch.cuda.Event() for _ in range(L)]
     pack_l = [src_bases[l:l + 1] for l in range(L)]
 
-    def forward_only(f_ev):
+    def forward_only(f_ev, rdy):
         with torch.cuda.stream(fwd):
             for _ in range(L):
                 torch.mm(a, b, out=c)
             f_ev.record(fwd)
 
-    def serial(f_ev):
+    def serial(f_ev, rdy):
         with torch.cuda.stream(fwd):
             for _ in range(L):
                 torch.mm(a, b, out=c)
             f_ev.record(fwd)
             K.kvx_pack(src_bases, BB, nb, xp, cp, N, buf, err, stream=fwd)
 
-    def pipelined(f_ev):
+    def inline(f_ev, rdy):
+        with torch.cuda.stream(fwd):
+            for l in range(L):
+                torch.mm(a, b, out=c)
+                if l == L - 1:
+                    f_ev.record(fwd)
+                K.kvx_pack(pack_l[l], BB, nb, xp, cp, N, bufv[l], err, stream=fwd)
+                K.kvx_signal_add(counter, 1, stream=fwd)
+                rdy[l].record(fwd)
+
+    def pipelined(f_ev, rdy):
         for l in range(L):
             with torch.cuda.stream(fwd):
                 torch.mm(a, b, out=c)
@@ -391,32 +406,42 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
             cpy.wait_event(evs[l])
             K.kvx_pack(pack_l[l], BB, nb, xp, cp, N, bufv[l], err, stream=cpy)
             K.kvx_signal_add(counter, 1, stream=cpy)
+            rdy[l].record(cpy)
         f_ev.record(fwd)
 
     def run(fn):
         torch.cuda.synchronize()
         s_ev, f_ev, e_ev = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        rdy = [torch.cuda.Event(enable_timing=True) for _ in range(L)]
         s_ev.record(fwd)
         cpy.wait_stream(fwd)
-        fn(f_ev)
+        fn(f_ev, rdy)
         fwd.wait_stream(cpy)
         e_ev.record(fwd)
         torch.cuda.synchronize()
-        return s_ev.elapsed_time(e_ev), f_ev.elapsed_time(e_ev)
+        total = s_ev.elapsed_time(e_ev)
+        # one launch packs every layer in the schedules without per-layer events: all of its
+        # layers are complete when it ends
+        ready = (sum(s_ev.elapsed_time(r) for r in rdy) / L) if fn in (inline, pipelined) else total
+        return total, f_ev.elapsed_time(e_ev), ready
 
     out = {"workload": f"{L} layers; forward stream: one bf16 [{m}x{k}]x[{k}x{k}] product per layer "
-                       "(forward stand-in); copy stream: that layer's pack, then a signal add"}
-    for name, fn in (("forward_only", forward_only), ("serial", serial), ("pipelined", pipelined)):
+                       "(forward stand-in); per layer: that layer's pack, then a signal add (inline on "
+                       "the forward stream, or pipelined on a copy stream)"}
+    for name, fn in (("forward_only", forward_only), ("serial", serial), ("inline", inline),
+                     ("pipelined", pipelined)):
         run(fn)  # warm
         ts = sorted(run(fn) for _ in range(reps))
-        total, tail = ts[len(ts) // 2]
+        total, tail, ready = ts[len(ts) // 2]
         out[f"{name}_ms"] = round(total, 4)
         if name != "forward_only":
             out[f"{name}_tail_ms"] = round(tail, 4)
-        log(f"layer pipeline {name}: {total:.4f} ms, tail after the forward {tail:.4f} ms")
+            out[f"{name}_mean_ready_ms"] = round(ready, 4)
+        log(f"layer pipeline {name}: {total:.4f} ms, tail after the forward {tail:.4f} ms, "
+            f"mean layer ready {ready:.4f} ms")
     torch.cuda.synchronize()
     assert int(err.item()) == 0, "device error flag raised"
-    assert int(counter.item()) == L * (reps + 1), "signal count"
+    assert int(counter.item()) == 2 * L * (reps + 1), "signal count"
     return out
 
 
@@ -507,11 +532,20 @@ def cpu_baseline(np, W, case, src_dev, table_h, req_h, pos_h, new_k_h, new_v_h, 
         cores_avail = len(os.sched_getaffinity(0))
     except AttributeError:
         cores_avail = os.cpu_count()
+    cpu_model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(nbytes / t_oracle / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"the oracle's step on {len(layers)} of {spec.num_layers} layers: both run lists and the "
                       f"slot mapping once, then per layer pack, unpack and the new-token write "
-                      f"({nbytes} algorithmic bytes, {t_oracle:.2f} s; numpy, single thread, "
-                      f"{cores_avail} host cores available)"}
+                      f"({nbytes} algorithmic bytes, {t_oracle:.2f} s; numpy, single thread: 1 of "
+                      f"{cores_avail} host cores available, {os.cpu_count()} online, {cpu_model})"}
 
 
 if __name__ == "__main__":

@@ -120,8 +120,23 @@ def _stream(stream) -> Optional[int]:
     import torch
 
     if stream is None:
+        # the raw handle of the current device's current stream, without building a Stream
+        # object (a third of a small call's host time otherwise)
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return raw(torch._C._cuda_getDevice())
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _rows_contiguous(t) -> bool:
+    """Every t[i] is densely packed (the dimensions after the first are contiguous)."""
+    expect = 1
+    for size, stride in zip(reversed(t.shape[1:]), reversed(t.stride()[1:])):
+        if size != 1 and stride != expect:
+            return False
+        expect *= size
+    return True
 
 
 def _want(t, dtype, name):
@@ -231,9 +246,9 @@ def kvx_reshape_and_cache(key, value, slot_mapping, kv_cache, num_blocks: int, b
     if key.shape[0] != T or value.shape[0] != T or key.shape != value.shape:
         raise ValueError("kvx: key/value must be [num_tokens, ...] of the same shape")
     e = key.element_size()
-    row = key[0].numel() * e if T else 0
+    row = key.numel() // T * e if T else 0
     for name, t in (("key", key), ("value", value)):
-        if T and not t[0].is_contiguous():
+        if not _rows_contiguous(t):
             raise ValueError(f"kvx: each {name} row must be contiguous")
     st = _F["kvx_reshape_and_cache"](_ptr(key), key.stride(0) * e, _ptr(value), value.stride(0) * e,
                                      T, row, _ptr(slot_mapping), _ptr(kv_cache), int(num_blocks),
