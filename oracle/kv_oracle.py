@@ -263,7 +263,7 @@ def unpack(src_buffers: Sequence[np.ndarray], dst_caches: Sequence[np.ndarray],
     nb, bb = out[0].shape
     order = buffer_order(dst_tables)
     N = len(order)
-    bufs = [np.ascontiguousarray(b).reshape(L, N, -1).view(np.uint8) for b in src_buffers]
+    bufs = [np.ascontiguousarray(b).reshape(-1).view(np.uint8).reshape(L, N, bb // S) for b in src_buffers]
     err = 0
     for l in range(L):
         for r, j, p in order:
@@ -359,7 +359,7 @@ def unpack_kv_first(buf: np.ndarray, dst_caches: Sequence[np.ndarray],
     L = len(out)
     _, nb, seg = out[0].shape
     N = sum(len(t) for t in dst_tables)
-    src = np.ascontiguousarray(buf).reshape(L, 2 * N, -1).view(np.uint8)
+    src = np.ascontiguousarray(buf).reshape(-1).view(np.uint8).reshape(L, 2 * N, seg)
     err = 0
     for l in range(L):
         at = 0

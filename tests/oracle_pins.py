@@ -561,4 +561,31 @@ def pin_split_then_merge_is_pack(o):
             assert np.array_equal(merged[l], plain[l])
 
 
+def pin_empty_transfer(o):
+    """No listed block (no requests, or only empty ones): no runs, an empty buffer, and every
+    receiving cache keeps its bytes, in every copy form."""
+    rng = np.random.default_rng(41)
+    src = [W.random_words(rng, (12, 64)) for _ in range(2)]
+    dst = [W.random_words(rng, (12, 64)) for _ in range(2)]
+    for tables in ([], [np.zeros(0, np.int32), np.zeros(0, np.int32)]):
+        for mode in (o.MODE_PACK, o.MODE_UNPACK, o.MODE_DIRECT):
+            assert o.xfer_list(tables, tables, mode) == []
+        buf, err = o.pack(src, tables)
+        assert err == 0 and buf.shape == (2, 0, 128)
+        out, err = o.unpack([buf], dst, tables)
+        assert err == 0 and all(np.array_equal(a, b.view(np.uint8)) for a, b in zip(out, dst))
+        out, err = o.copy_direct(src, dst, tables, tables)
+        assert err == 0 and all(np.array_equal(a, b.view(np.uint8)) for a, b in zip(out, dst))
+        kplanes = [c.reshape(2, 12, 32) for c in src]
+        dplanes = [c.reshape(2, 12, 32) for c in dst]
+        kbuf, err = o.pack_kv_first(kplanes, tables)
+        assert err == 0 and kbuf.shape == (2, 0, 64)
+        out, err = o.unpack_kv_first(kbuf, dplanes, tables)
+        assert err == 0 and all(np.array_equal(a, b.view(np.uint8)) for a, b in zip(out, dplanes))
+        shards, err = o.pack_split(src, tables, 2, rows_per_block=4)
+        assert err == 0 and [s.shape for s in shards] == [(2, 0, 64)] * 2
+        out, err = o.unpack(shards, dst, tables, rows_per_block=4)
+        assert err == 0 and all(np.array_equal(a, b.view(np.uint8)) for a, b in zip(out, dst))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
