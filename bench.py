@@ -352,7 +352,9 @@ def main():
 def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, reps):
     """The sender's side of a layer-pipelined transfer. One bf16 [8192 x 4096] x [4096 x 4096]
     product per layer on the forward stream stands in for that layer's forward pass (it is not
-    part of the path). Schedules, each timed from a start event to the end of all streams:
+    part of the path): each layer has its own weight, and its output is the next layer's input,
+    so no layer finds the previous layer's operands in cache. Schedules, each timed from a start
+    event to the end of all streams:
       forward_only  the 48 products;
       serial        the 48 products, then one pack of all layers on the forward stream;
       inline        per layer on the forward stream: the product, the pack of that layer into
@@ -366,9 +368,12 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
     layers: when a transport could begin sending each layer). The receiver's unpack is left
     out: it runs on the other GPU of a real transfer, not beside the sender's forward pass."""
     m, k = 8192, 4096
-    a = torch.full((m, k), 0.5, dtype=torch.bfloat16, device=dev)
-    b = torch.full((k, k), 0.25, dtype=torch.bfloat16, device=dev)
-    c = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    # activations stay 0.5 exactly: each output element is k * 0.5 * 2^-12
+    acts = [torch.full((m, k), 0.5, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    weights = torch.full((L, k, k), 2.0 ** -12, dtype=torch.bfloat16, device=dev)
+
+    def layer_forward(l):
+        torch.mm(acts[l % 2], weights[l], out=acts[(l + 1) % 2])
     fwd, cpy = torch.cuda.Stream(), torch.cuda.Stream()
     counter = torch.zeros(1, dtype=torch.int64, device=dev)
     bufv = buf[: L * N * BB].view(L, N, BB)
@@ -377,21 +382,21 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
 
     def forward_only(f_ev, rdy):
         with torch.cuda.stream(fwd):
-            for _ in range(L):
-                torch.mm(a, b, out=c)
+            for l in range(L):
+                layer_forward(l)
             f_ev.record(fwd)
 
     def serial(f_ev, rdy):
         with torch.cuda.stream(fwd):
-            for _ in range(L):
-                torch.mm(a, b, out=c)
+            for l in range(L):
+                layer_forward(l)
             f_ev.record(fwd)
             K.kvx_pack(src_bases, BB, nb, xp, cp, N, buf, err, stream=fwd)
 
     def inline(f_ev, rdy):
         with torch.cuda.stream(fwd):
             for l in range(L):
-                torch.mm(a, b, out=c)
+                layer_forward(l)
                 if l == L - 1:
                     f_ev.record(fwd)
                 K.kvx_pack(pack_l[l], BB, nb, xp, cp, N, bufv[l], err, stream=fwd)
@@ -401,7 +406,7 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
     def pipelined(f_ev, rdy):
         for l in range(L):
             with torch.cuda.stream(fwd):
-                torch.mm(a, b, out=c)
+                layer_forward(l)
                 evs[l].record(fwd)
             cpy.wait_event(evs[l])
             K.kvx_pack(pack_l[l], BB, nb, xp, cp, N, bufv[l], err, stream=cpy)
@@ -425,9 +430,10 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
         ready = (sum(s_ev.elapsed_time(r) for r in rdy) / L) if fn in (inline, pipelined) else total
         return total, f_ev.elapsed_time(e_ev), ready
 
-    out = {"workload": f"{L} layers; forward stream: one bf16 [{m}x{k}]x[{k}x{k}] product per layer "
-                       "(forward stand-in); per layer: that layer's pack, then a signal add (inline on "
-                       "the forward stream, or pipelined on a copy stream)"}
+    out = {"workload": f"{L} layers; forward stream: one bf16 [{m}x{k}]x[{k}x{k}] product per layer with "
+                       "its own weight, output feeding the next layer (forward stand-in); per layer: that "
+                       "layer's pack, then a signal add (inline on the forward stream, or pipelined on a "
+                       "copy stream)"}
     for name, fn in (("forward_only", forward_only), ("serial", serial), ("inline", inline),
                      ("pipelined", pipelined)):
         run(fn)  # warm
