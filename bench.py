@@ -17,7 +17,7 @@ One step = one pass of the whole hot path over that batch:
 Under "ops", each after evicting the Infinity Cache: the same caches as kv-first views, the
 direct cache-to-cache copy, the layer-pipelined pack beside a GEMM forward stand-in, the
 asymmetric-TP head merge and split (32 layers, 64 KiB blocks), and the 32-request decode
-slot mapping and new-token write. "cpu_baseline" is the CPU oracle on the whole step.
+slot mapping and new-token write (rows of 8 heads, 2 KiB, and of 1 head, 256 B). "cpu_baseline" is the CPU oracle on the whole step.
 "graph_ms_per_step" is the same step captured once in a HIP graph and replayed (`value`
 stays the eager rate: a graph is fixed to one transfer size).
 
@@ -502,6 +502,20 @@ def other_workloads(torch, np, W, K, dev, flush, reps):
         "tokens": T, "bytes": wbytes, "median_ms": round(med, 5),
         "GB/s": round(wbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(wbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "traffic": traffic_from_counters("write_decode", wbytes)}
+    del cache, key, val
+    # the same tokens with the 48-layer caches' rows: 1 head x 128 bf16 = 256 B per K or V row
+    d1 = W.decode_write(num_kv_heads=1)
+    cache1 = torch.full(d1.spec.shape5, -1, dtype=torch.int16, device=dev)
+    key1, val1 = torch.from_numpy(d1.key).to(dev), torch.from_numpy(d1.value).to(dev)
+    cnb, cbs, bst, tst, kst = K.cache_strides(cache1)
+    med, mn = time_op(torch, lambda: K.kvx_reshape_and_cache(key1, val1, slots, cache1, cnb, cbs, bst, tst, kst),
+                      reps, flush)
+    wbytes = T * (4 * d1.spec.row_bytes + 8)
+    out["reshape_and_cache_decode_1head"] = {
+        "workload": f"the same {T} tokens and slots, rows of 1 head x 128 bf16 (256 B) into [4096][16][K,V][1][128]",
+        "tokens": T, "bytes": wbytes, "median_ms": round(med, 5),
+        "GB/s": round(wbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(wbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "traffic": traffic_from_counters("write_decode_1head", wbytes)}
     return out
 
 
