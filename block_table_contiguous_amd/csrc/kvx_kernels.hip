@@ -47,6 +47,7 @@ const Tuning& tuning() {
       (int)env_i64("KVX_XCD_REMAP", 1),
       (int)env_i64("KVX_ONE_BATCH", 1),
       (int)env_i64("KVX_NT_WRITE", 1),
+      env_i64("KVX_WRITE_VEC_MIN", 4096),
   };
   return t;
 }
@@ -222,6 +223,73 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
 // a2 — new-token K/V write: K row and V row of each token into its slot
 // --------------------------------------------------------------------------------------
 
+// New-token write, one wavefront per token (K row and V row in one pass): the shortest
+// dependency chain per token, for launches too small to fill the chip. Rows need only be a
+// multiple of 16 bytes.
+template <int K>
+__global__ __launch_bounds__(256) void write_tokens_kernel(
+    const char* __restrict__ key, int64_t key_stride, const char* __restrict__ value,
+    int64_t value_stride, int64_t num_tokens, int64_t row_bytes,
+    const int64_t* __restrict__ slots, char* __restrict__ cache, int64_t num_blocks,
+    int32_t block_size, int64_t block_stride, int64_t token_stride, int64_t kv_stride,
+    int32_t* err) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t waves_per_wg = blockDim.x / kWave;
+  const int64_t wave = uniform((int64_t)blockIdx.x * waves_per_wg + (threadIdx.x / kWave));
+  const int64_t num_waves = (int64_t)gridDim.x * waves_per_wg;
+  const int64_t nvec = row_bytes / kVec;  // vectors in one row
+  const int64_t nv2 = 2 * nvec;           // vector q < nvec is in the K row, else in the V row
+  const KVX_CONST int64_t* sl = readonly(slots);
+  for (int64_t t = wave; t < num_tokens; t += num_waves) {
+    const char* krow = key + t * key_stride;
+    const char* vrow = value + t * value_stride;
+    // The rows do not depend on the slot: their first batch is in flight before the slot
+    // arrives. Lanes past the rows re-read vector 0 so every load is unconditional.
+    u32x4 v[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      int64_t q = (int64_t)j * kWave + lane;
+      q = q < nv2 ? q : 0;
+      v[j] = load16<false>(q < nvec ? krow + q * kVec : vrow + (q - nvec) * kVec);
+    }
+    const int64_t s = sl[t];
+    if (s < 0) continue;  // padding token
+    int64_t blk, off;
+    if (s <= 0x7fffffff) {
+      blk = (uint32_t)s / (uint32_t)block_size;
+      off = (uint32_t)s - (uint32_t)blk * (uint32_t)block_size;
+    } else {
+      blk = s / block_size;
+      off = s - blk * block_size;
+    }
+    if (blk >= num_blocks) {
+      if (lane == 0) raise_error(err, KVX_DEVERR_SLOT_RANGE);
+      continue;
+    }
+    char* kdst = cache + blk * block_stride + off * token_stride;
+    char* vdst = kdst + kv_stride;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const int64_t q = (int64_t)j * kWave + lane;
+      if (q < nv2) store16<false>(q < nvec ? kdst + q * kVec : vdst + (q - nvec) * kVec, v[j]);
+    }
+    // rows longer than one batch (over K*64 vectors for K and V together)
+    for (int64_t q0 = (int64_t)K * kWave; q0 < nv2; q0 += (int64_t)K * kWave) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        int64_t q = q0 + j * kWave + lane;
+        q = q < nv2 ? q : 0;
+        v[j] = load16<false>(q < nvec ? krow + q * kVec : vrow + (q - nvec) * kVec);
+      }
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int64_t q = q0 + j * kWave + lane;
+        if (q < nv2) store16<false>(q < nvec ? kdst + q * kVec : vdst + (q - nvec) * kVec, v[j]);
+      }
+    }
+  }
+}
+
 struct WriteArgs {
   const char* key;
   const char* value;
@@ -231,8 +299,10 @@ struct WriteArgs {
   int64_t key_stride, value_stride;
   int64_t num_tokens, row_bytes, num_blocks;
   int64_t block_stride, token_stride, kv_stride;
-  int64_t total_slots;  // num_tokens * 2 * row KiB
+  int64_t total_slots;      // whole-KiB kernel: num_tokens * 2 * row KiB
   int32_t block_size;
+  int32_t block_shift;      // vector kernel: log2(block_size) if a power of two, else -1
+  int32_t tokens_per_wave;  // vector kernel: whole tokens per wavefront
 };
 
 // New-token write when a row is a multiple of 1 KiB. The (token, K/V, KiB of row) sequence
@@ -311,46 +381,56 @@ __global__ __launch_bounds__(256) void write_slots_kernel(WriteArgs a) {
   if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_SLOT_RANGE);
 }
 
-// New-token write for rows that are not whole KiB (any multiple of 16 bytes). The
-// (token, K/V, 16-byte vector) sequence is cut into batches of kWriteSlots * 64 vectors, one
-// batch per wavefront: lane l of instruction j takes vector base + 64 j + l. A token spans
-// 2 * row / 16 consecutive vectors, so 256-byte rows put 16 tokens in one wavefront instead
-// of one. Each lane's row loads and slot loads are all in flight before its stores.
+// New-token write for rows of up to 4 KiB that are not whole KiB (any multiple of 16 bytes).
+// A wavefront takes tokens_per_wave whole tokens (as many as fit in kWriteSlots * 64 vectors:
+// 16 tokens of 256-byte rows); lane l of instruction j takes vector 64 j + l of that run of
+// (token, K/V, 16-byte vector) triples. Each lane's row loads and slot loads are all in flight
+// before its stores. Indexing is by additions from one small division per lane, so a launch
+// of a few tokens costs little more than its memory latency.
 template <bool NTL, bool NTS>
 __global__ __launch_bounds__(256) void write_vectors_kernel(WriteArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t w = uniform((int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave));
-  const int64_t nvec = a.row_bytes / kVec;  // vectors per row
-  const int64_t tv = 2 * nvec;              // vectors per token: the K row, then the V row
-  const int64_t total = a.num_tokens * tv;
-  const int64_t g0 = w * ((int64_t)kWriteSlots * kWave);
-  if (g0 >= total) return;
-  // Lane's vector as (token t, index r inside the token); each instruction moves the index
-  // on by 64 vectors = step_t tokens + step_r vectors.
-  const int64_t step_t = kWave / tv;
-  const int64_t step_r = kWave - step_t * tv;
-  int64_t g = g0 + lane;
-  int64_t t = g / tv;
-  int64_t r = g - t * tv;
+  const int64_t t0 = w * a.tokens_per_wave;
+  if (t0 >= a.num_tokens) return;
+  const int64_t t_end = t0 + a.tokens_per_wave < a.num_tokens ? t0 + a.tokens_per_wave : a.num_tokens;
+  const uint32_t nvec = (uint32_t)(a.row_bytes / kVec);  // vectors per row
+  const uint32_t tv = 2 * nvec;  // vectors per token (K row, then V row), at most 512
+  // lane's vector as (token t, index r inside the token); each instruction moves on by 64
+  // vectors = step_t tokens + step_r vectors
+  const uint32_t step_t = kWave / tv, step_r = kWave - step_t * tv;
+  const uint32_t tl = (uint32_t)lane / tv;
+  uint32_t r = (uint32_t)lane - tl * tv;
+  int64_t t = t0 + tl;
+  const char* kp = a.key + t * a.key_stride;
+  const char* vp = a.value + t * a.value_stride;
+  const int64_t* slot_p = a.slots + t;
+  const int64_t dk = (int64_t)step_t * a.key_stride, dv = (int64_t)step_t * a.value_stride;
 
   const char* sp[kWriteSlots];
-  int64_t tok[kWriteSlots], dof[kWriteSlots];
+  const int64_t* slp[kWriteSlots];
+  int64_t dof[kWriteSlots];
   bool live[kWriteSlots];
 #pragma unroll
   for (int j = 0; j < kWriteSlots; ++j) {
-    live[j] = g < total;
+    live[j] = t < t_end;
     const bool is_v = r >= nvec;
-    const int64_t q = is_v ? r - nvec : r;
-    tok[j] = live[j] ? t : 0;
-    dof[j] = (is_v ? a.kv_stride : 0) + q * kVec;  // offset inside the token's slot
-    sp[j] = live[j] ? (is_v ? a.value + t * a.value_stride : a.key + t * a.key_stride) + q * kVec
-                    : a.key;  // idle lanes re-read the first vector of row 0
-    g += kWave;
+    const uint32_t q = is_v ? r - nvec : r;
+    dof[j] = (is_v ? a.kv_stride : 0) + (int64_t)q * kVec;  // offset inside the token's slot
+    // idle lanes re-read the first vector of row 0 and slot 0
+    sp[j] = live[j] ? (is_v ? vp : kp) + (int64_t)q * kVec : a.key;
+    slp[j] = live[j] ? slot_p : a.slots;
     t += step_t;
+    kp += dk;
+    vp += dv;
+    slot_p += step_t;
     r += step_r;
     if (r >= tv) {
       r -= tv;
       ++t;
+      kp += a.key_stride;
+      vp += a.value_stride;
+      ++slot_p;
     }
   }
   u32x4 v[kWriteSlots];
@@ -358,11 +438,12 @@ __global__ __launch_bounds__(256) void write_vectors_kernel(WriteArgs a) {
   for (int j = 0; j < kWriteSlots; ++j) v[j] = load16<NTL>(sp[j]);
   int64_t sv[kWriteSlots];
 #pragma unroll
-  for (int j = 0; j < kWriteSlots; ++j) sv[j] = a.slots[tok[j]];
+  for (int j = 0; j < kWriteSlots; ++j) sv[j] = *slp[j];
 
   char* dp[kWriteSlots];
   bool on[kWriteSlots];
   bool bad = false;
+  const int32_t shift = a.block_shift;
 #pragma unroll
   for (int j = 0; j < kWriteSlots; ++j) {
     const int64_t s = sv[j];
@@ -370,7 +451,10 @@ __global__ __launch_bounds__(256) void write_vectors_kernel(WriteArgs a) {
     dp[j] = a.cache;
     if (live[j] && s >= 0) {
       int64_t blk, off;
-      if (s <= 0x7fffffff) {
+      if (shift >= 0) {
+        blk = s >> shift;
+        off = s & (((int64_t)1 << shift) - 1);
+      } else if (s <= 0x7fffffff) {
         blk = (uint32_t)s / (uint32_t)a.block_size;
         off = (uint32_t)s - (uint32_t)blk * (uint32_t)a.block_size;
       } else {
@@ -1199,6 +1283,15 @@ hipError_t launch_reshape_and_cache(const void* key, int64_t key_stride, const v
     }
     return hipGetLastError();
   }
+  const int64_t vec_per_token = 2 * (row_bytes / kVec);
+  if (num_tokens < tuning().write_vec_min || vec_per_token > (int64_t)kWriteSlots * kWave) {
+    const int64_t wgs = ceil_div(num_tokens, 4);
+    const unsigned grid = (unsigned)(wgs < (1 << 20) ? wgs : (1 << 20));
+    write_tokens_kernel<4><<<grid, 256, 0, stream>>>(
+        (const char*)key, key_stride, (const char*)value, value_stride, num_tokens, row_bytes,
+        slots, (char*)cache, num_blocks, block_size, block_stride, token_stride, kv_stride, err);
+    return hipGetLastError();
+  }
   WriteArgs a;
   a.key = (const char*)key;
   a.value = (const char*)value;
@@ -1214,9 +1307,10 @@ hipError_t launch_reshape_and_cache(const void* key, int64_t key_stride, const v
   a.token_stride = token_stride;
   a.kv_stride = kv_stride;
   a.block_size = block_size;
-  const int64_t total_vec = num_tokens * 2 * (row_bytes / kVec);
-  a.total_slots = 0;  // read by the whole-KiB kernel only
-  const int64_t wgs = ceil_div(ceil_div(total_vec, (int64_t)kWriteSlots * kWave), 4);
+  a.total_slots = 0;
+  a.block_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
+  a.tokens_per_wave = (int32_t)(((int64_t)kWriteSlots * kWave) / vec_per_token);
+  const int64_t wgs = ceil_div(ceil_div(num_tokens, (int64_t)a.tokens_per_wave), 4);
   if (wgs >= ((int64_t)1 << 31)) return hipErrorInvalidConfiguration;
   const unsigned grid = (unsigned)wgs;
   switch (tuning().write_nt & 3) {

@@ -23,6 +23,7 @@ struct Tuning {
   int xcd_remap;  // 1: give each XCD a contiguous slice of the work (KVX_XCD_REMAP)
   int one_batch;  // 1: one-batch-per-wavefront kernels where blocks allow (KVX_ONE_BATCH)
   int write_nt;   // cache policy of the new-token write, bits as nt_mode (KVX_NT_WRITE)
+  int64_t write_vec_min;  // fewest tokens for the vector-sliced write of sub-KiB rows (KVX_WRITE_VEC_MIN)
 };
 const Tuning& tuning();
 
