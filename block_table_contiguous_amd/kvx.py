@@ -229,8 +229,10 @@ def kvx_slot_mapping(block_table, req_idx, positions, block_size: int, slot_mapp
     if positions.numel() != T or slot_mapping.numel() != T:
         raise ValueError("kvx: req_idx, positions and slot_mapping need the same length")
     width = block_table.shape[1] if max_blocks_per_req is None else int(max_blocks_per_req)
+    # a one-row table's row stride is never used (it can be 0 for a broadcast row)
+    row_stride = block_table.stride(0) if block_table.shape[0] > 1 else max(block_table.shape[1], width)
     st = _F["kvx_slot_mapping"](_ptr(block_table), block_table.shape[0], width,
-                                block_table.stride(0), _ptr(req_idx), _ptr(positions), T,
+                                row_stride, _ptr(req_idx), _ptr(positions), T,
                                 int(block_size), _ptr(slot_mapping), _ptr(err_flag), _stream(stream))
     _check("kvx_slot_mapping", st)
 
