@@ -203,3 +203,29 @@ def test_copy_direct_validation(kvx):
     assert direct(nbs=0) == kvx.KVX_ERR_INVALID_ARGUMENT  # nothing to read from
     assert direct(bb=8200) == kvx.KVX_ERR_MISALIGNED
     assert direct(n=0, sb=None) == kvx.KVX_SUCCESS
+
+
+def _run_python(code, env_extra=None):
+    import subprocess
+    import sys
+
+    env = dict(os.environ)
+    env.update(env_extra or {})
+    return subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                          timeout=120)
+
+
+def test_binding_fails_loudly_without_the_library():
+    """No fallback: without the built library the binding refuses to import."""
+    r = _run_python("import block_table_contiguous_amd.kvx", {"KVX_SO_PATH": "/nonexistent/libkvx.so"})
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "no fallback" in r.stderr
+
+
+def test_product_path_never_imports_the_oracle():
+    """The package and its binding load without touching the oracle or the input generators."""
+    r = _run_python("import sys, block_table_contiguous_amd, block_table_contiguous_amd.kvx, "
+                    "block_table_contiguous_amd.build; "
+                    "bad = [m for m in sys.modules if m == 'oracle' or m.startswith('oracle.') or m == 'workloads']; "
+                    "print(bad); sys.exit(1 if bad else 0)")
+    assert r.returncode == 0, r.stdout + r.stderr
