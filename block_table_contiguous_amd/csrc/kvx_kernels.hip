@@ -1003,11 +1003,14 @@ __global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(RunCopyArgs a)
   if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_BLOCK_RANGE);
 }
 
-// Head shards when a row piece is a multiple of 1 KiB. Wavefront w owns K KiB of one
-// layer's cache-side bytes taken in buffer order (position q, then row, then shard, then
-// byte); slot j is the 1 KiB at offset w_in of the cache block for position q, which is
-// bytes [xo, xo + 1 KiB) of row `row` of shard d. Counters step (xo, d, row, q) without
-// divisions. TO_BUFFER = split (cache -> shards), otherwise merge (shards -> cache).
+// Head shards when a row piece is a multiple of 1 KiB. TO_BUFFER = split (cache -> shards),
+// otherwise merge (shards -> cache). Wavefront w owns K KiB of one layer's bytes, taken in
+// the order that makes its stores contiguous: for the merge the cache side's order (position
+// q, then row, then shard, then byte: slot j is the 1 KiB at offset w_in of the cache block),
+// for the split the shard side's order (q, then shard, then row, then byte: slot j is the
+// 1 KiB at offset w_in of the position's bytes in shard d). Either way slot j is bytes
+// [xo, xo + 1 KiB) of row `row` of shard d, and counters step without divisions. The split's
+// order was 1% faster than the cache side's in interleaved A/B runs.
 template <bool TO_BUFFER, bool NTL, bool NTS, int K>
 __global__ __launch_bounds__(kCopyThreads) void shard_slots_kernel(ShardArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -1030,13 +1033,23 @@ __global__ __launch_bounds__(kCopyThreads) void shard_slots_kernel(ShardArgs a) 
   if (count <= 0) return;
   char* cache = const_cast<char*>(*readonly(a.layer_bases + l));
 
+  constexpr bool kShardOrder = TO_BUFFER;
+  const int64_t rows = BBs / piece;
   const int64_t o0 = u * ((int64_t)K * kWaveBytes);
   int64_t q = o0 / BB;
   int64_t w_in = o0 - q * BB;
-  int64_t row = w_in / row_full;
-  int64_t rem = w_in - row * row_full;
-  int64_t d = rem / piece;
-  int64_t xo = rem - d * piece;
+  int64_t row, d, xo;
+  if (kShardOrder) {
+    d = w_in / BBs;
+    const int64_t rem = w_in - d * BBs;
+    row = rem / piece;
+    xo = rem - row * piece;
+  } else {
+    row = w_in / row_full;
+    const int64_t rem = w_in - row * row_full;
+    d = rem / piece;
+    xo = rem - d * piece;
+  }
   int64_t k = uniform(find_run(a.xfers, count, q, lane));
   if (k < 0) k = 0;
   Run x = load_run(xf, k);
@@ -1058,7 +1071,7 @@ __global__ __launch_bounds__(kCopyThreads) void shard_slots_kernel(ShardArgs a) 
         const int64_t id = (TO_BUFFER ? x.src : x.dst) + (q - x.buf);
         if (id >= 0 && id < a.num_cache_blocks) {
           char* sh = a.shard[d] + (l * N + q) * BBs + row * piece + xo;
-          char* ca = cache + id * BB + w_in;
+          char* ca = cache + id * BB + (kShardOrder ? row * row_full + d * piece + xo : w_in);
           sp[j] = TO_BUFFER ? ca : sh;
           dp[j] = TO_BUFFER ? sh : ca;
           on[j] = true;
@@ -1071,7 +1084,11 @@ __global__ __launch_bounds__(kCopyThreads) void shard_slots_kernel(ShardArgs a) 
     w_in += kWaveBytes;
     if (xo == piece) {
       xo = 0;
-      if (++d == S) { d = 0; ++row; }
+      if (kShardOrder) {
+        if (++row == rows) { row = 0; ++d; }
+      } else {
+        if (++d == S) { d = 0; ++row; }
+      }
     }
     if (w_in == BB) { w_in = 0; row = 0; d = 0; xo = 0; ++q; }
   }
