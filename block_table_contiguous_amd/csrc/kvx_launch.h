@@ -21,6 +21,7 @@ struct CopyTuning {
 struct Tuning {
   CopyTuning pack, unpack, merge, split, kvf_pack, kvf_unpack, direct;
   int xcd_remap;  // 1: give each XCD a contiguous slice of the work (KVX_XCD_REMAP)
+  int xcd_remap_split;  // the same for the head split (KVX_XCD_REMAP_SPLIT)
   int one_batch;  // 1: one-batch-per-wavefront kernels where blocks allow (KVX_ONE_BATCH)
   int write_nt;   // cache policy of the new-token write, bits as nt_mode (KVX_NT_WRITE)
   int64_t write_vec_min;  // fewest tokens for the vector-sliced write of sub-KiB rows (KVX_WRITE_VEC_MIN)
