@@ -16,8 +16,7 @@ Sources (the four pages this path is built from):
             destination addresses; TP heterogeneity) and §七 item 3 (destination address =
             per-layer base + block length x block id).
 
-Readings where the pages are silent or garbled are listed in the design notes and
-repeated at each function.
+Readings where the pages are silent or garbled are stated at each function.
 
 Every function works on raw bytes and returns new arrays (inputs are never modified).
 Device-side error bits are mirrored so error cases can be compared too.
