@@ -44,6 +44,19 @@ def _as_block_bytes(cache: np.ndarray) -> np.ndarray:
     return c.reshape(c.shape[0], -1).view(np.uint8)
 
 
+def _reject_repeats(targets, what: str) -> None:
+    """Raise ValueError if any target appears twice. Reading (the pages' receiver allocates
+    fresh blocks for every request, [pd] §三 3.2): two entries that would write the same
+    destination block or slot are invalid input, not a case with a defined winner, so the
+    oracle refuses them instead of choosing one. Targets outside the cache are not writes
+    (they are skipped and flagged) and are not passed here."""
+    seen = set()
+    for t in targets:
+        if t in seen:
+            raise ValueError(f"{what} {t} is written twice: destinations must be distinct")
+        seen.add(t)
+
+
 def buffer_order(tables: Sequence[np.ndarray]) -> List[Tuple[int, int, int]]:
     """The flat request-major order of all listed blocks: (request r, index j in r's table,
     position p). Position p = (blocks of requests before r) + j; this is where block j of
@@ -115,9 +128,12 @@ def reshape_and_cache(cache: np.ndarray, key_rows: np.ndarray, value_rows: np.nd
     kv_stride = row_bytes, block_stride = block_size*token_stride.
 
     Reading: a negative slot means "no slot" (a padding token) and is skipped; a slot in a
-    block >= num_blocks is skipped and raises DEVERR_SLOT_RANGE. Tokens are applied in
-    order. Returns (new cache bytes, flat uint8, error bits).
+    block >= num_blocks is skipped and raises DEVERR_SLOT_RANGE. Two tokens with the same
+    slot inside the cache are invalid input (ValueError), since each new token owns its slot.
+    Returns (new cache bytes, flat uint8, error bits).
     """
+    _reject_repeats([int(s) for s in slots if int(s) >= 0 and int(s) // block_size < num_blocks],
+                    "slot")
     out = np.ascontiguousarray(cache).reshape(-1).view(np.uint8).copy()
     K = np.ascontiguousarray(key_rows).reshape(len(slots), -1).view(np.uint8)
     V = np.ascontiguousarray(value_rows).reshape(len(slots), -1).view(np.uint8)
@@ -252,8 +268,9 @@ def unpack(src_buffers: Sequence[np.ndarray], dst_caches: Sequence[np.ndarray],
     tensor into kv_cache_layer[block_ids]); [pd] §七 item 3 (destination = layer base +
     block length x block id); [pd] §四 4.2 (TP heterogeneity).
 
-    Reading: destination ids are unique (the receiver allocates fresh blocks); a
-    destination id outside [0, num_blocks) is skipped and raises DEVERR_BLOCK_RANGE.
+    Reading: a destination id outside [0, num_blocks) is skipped and raises
+    DEVERR_BLOCK_RANGE; a destination id inside the cache listed twice is invalid input
+    (ValueError), since the receiver allocates fresh blocks.
     Returns (new destination caches as [num_blocks][block_bytes] uint8, error bits).
     """
     S = len(src_buffers)
@@ -261,6 +278,8 @@ def unpack(src_buffers: Sequence[np.ndarray], dst_caches: Sequence[np.ndarray],
     L = len(out)
     nb, bb = out[0].shape
     order = buffer_order(dst_tables)
+    _reject_repeats([int(dst_tables[r][j]) for r, j, _ in order if 0 <= int(dst_tables[r][j]) < nb],
+                    "destination block")
     N = len(order)
     bufs = [np.ascontiguousarray(b).reshape(-1).view(np.uint8).reshape(L, N, bb // S) for b in src_buffers]
     err = 0
@@ -288,12 +307,14 @@ def copy_direct(src_caches: Sequence[np.ndarray], dst_caches: Sequence[np.ndarra
     §七 item 3 (address = layer base + block length x block id).
 
     Reading: an entry whose source or destination id is outside its cache is not copied
-    and raises DEVERR_BLOCK_RANGE (pack's rule for sources, unpack's for destinations).
+    and raises DEVERR_BLOCK_RANGE (pack's rule for sources, unpack's for destinations); a
+    destination id inside the cache listed twice is invalid input (ValueError), as for unpack.
     Returns (new destination caches as [num_blocks][block_bytes] uint8, error bits).
     """
     srcs = [_as_block_bytes(c) for c in src_caches]
     out = [_as_block_bytes(c).copy() for c in dst_caches]
     nbs, nbd = srcs[0].shape[0], out[0].shape[0]
+    _reject_repeats([int(d) for t in dst_tables for d in t if 0 <= int(d) < nbd], "destination block")
     err = 0
     for l in range(len(out)):
         for r in range(len(src_tables)):
@@ -353,10 +374,12 @@ def unpack_kv_first(buf: np.ndarray, dst_caches: Sequence[np.ndarray],
     """Inverse of pack_kv_first into the receiver's kv-first caches: request r's K segments
     go to plane 0 of its destination blocks in table order, then its V segments to plane 1.
     [nccl] §2.3 step 14 / §2.4 (inject_kv_into_layer). Unlisted blocks keep their bytes;
-    out-of-range destination ids are skipped and raise DEVERR_BLOCK_RANGE."""
+    out-of-range destination ids are skipped and raise DEVERR_BLOCK_RANGE; an in-range
+    destination id listed twice is invalid input (ValueError), as for unpack."""
     out = [_planes(c).copy() for c in dst_caches]
     L = len(out)
     _, nb, seg = out[0].shape
+    _reject_repeats([int(d) for t in dst_tables for d in t if 0 <= int(d) < nb], "destination block")
     N = sum(len(t) for t in dst_tables)
     src = np.ascontiguousarray(buf).reshape(-1).view(np.uint8).reshape(L, 2 * N, seg)
     err = 0

@@ -126,18 +126,59 @@ def pin_reshape_kv_first_layout(o):
 
 
 def pin_reshape_padding_and_range(o):
-    """Negative slots are skipped silently; slots past the cache are skipped and flagged;
-    later tokens overwrite earlier ones in token order."""
+    """Negative slots are skipped silently (also when repeated); slots past the cache are
+    skipped and flagged (also when repeated); every other token lands in its own slot."""
     cache = np.zeros((4, 2, 2, 1, 8), np.uint16)  # 4 blocks of 2 tokens, row = 16 B
-    key = np.arange(4 * 8, dtype=np.uint16).reshape(4, 1, 8) + 1
+    key = np.arange(5 * 8, dtype=np.uint16).reshape(5, 1, 8) + 1
     val = key + 100
-    slots = [-1, 8, 3, 3]
+    slots = [-1, 8, 3, 8, -1]
     out, err = o.reshape_and_cache(cache, key, val, slots, 4, 2, 64, 32, 16)
     v = out.view(np.uint16).reshape(4, 2, 2, 1, 8)
     assert err == o.DEVERR_SLOT_RANGE
-    assert np.array_equal(v[1, 1, 0], key[3]) and np.array_equal(v[1, 1, 1], val[3])
+    assert np.array_equal(v[1, 1, 0], key[2]) and np.array_equal(v[1, 1, 1], val[2])
     v[1, 1] = 0
     assert not v.any()
+
+
+def _raises_value_error(fn):
+    try:
+        fn()
+    except ValueError:
+        return True
+    return False
+
+
+def pin_repeated_destinations_rejected(o):
+    """Two entries that would write the same destination block (or slot) inside the cache
+    are invalid input and every writing step refuses them, because a receiver allocates a
+    fresh block for every listed block ("vLLM PD 分离" §三 3.2): no step picks a winner.
+    Ids outside the cache are not writes, so repeating them is still allowed."""
+    cache = np.zeros((4, 2, 2, 1, 8), np.uint16)
+    key = np.ones((2, 1, 8), np.uint16)
+    assert _raises_value_error(lambda: o.reshape_and_cache(cache, key, key, [3, 3], 4, 2, 64, 32, 16))
+    assert _raises_value_error(lambda: o.reshape_and_cache(cache, key, key, [7, 7], 4, 2, 64, 32, 16))
+    _, err = o.reshape_and_cache(cache, key, key, [8, 8], 4, 2, 64, 32, 16)
+    assert err == o.DEVERR_SLOT_RANGE
+    buf = np.arange(3 * 16, dtype=np.uint8).reshape(1, 3, 16)
+    recv = [np.zeros((4, 16), np.uint8)]
+    same_req = [np.array([2, 0, 2])]
+    two_reqs = [np.array([1, 2]), np.array([2])]
+    for tables in (same_req, two_reqs):
+        assert _raises_value_error(lambda: o.unpack([buf], recv, tables))
+        halves = [buf[:, :, :8], buf[:, :, 8:]]
+        assert _raises_value_error(lambda: o.unpack(halves, recv, tables, rows_per_block=1))
+        src_tables = [np.arange(len(t)) for t in tables]
+        assert _raises_value_error(lambda: o.copy_direct([np.zeros((4, 16), np.uint8)], recv, src_tables, tables))
+        kvf_buf = np.zeros((1, 6, 1024), np.uint8)
+        kvf_recv = [np.zeros((2, 4, 1024), np.uint8)]
+        assert _raises_value_error(lambda: o.unpack_kv_first(kvf_buf, kvf_recv, tables))
+    out, err = o.unpack([buf], recv, [np.array([-1, 4, -1])])
+    assert err == o.DEVERR_BLOCK_RANGE and not out[0].any()
+    out, err = o.copy_direct([np.ones((4, 16), np.uint8)], recv, [np.array([0, 1, 2])], [np.array([4, 1, 4])])
+    assert err == o.DEVERR_BLOCK_RANGE and out[0][1].all() and not out[0][[0, 2, 3]].any()
+    out, err = o.unpack_kv_first(np.ones((1, 6, 1024), np.uint8), [np.zeros((2, 4, 1024), np.uint8)],
+                                 [np.array([-1, 0, -1])])
+    assert err == o.DEVERR_BLOCK_RANGE and out[0][:, 0].all() and not out[0][:, 1:].any()
 
 
 # --------------------------------------------------------------------------- runs

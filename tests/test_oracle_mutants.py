@@ -54,6 +54,18 @@ MUTANTS = [
     ("split_rows_transposed", "b[k * row + d * piece:k * row + (d + 1) * piece]",
      "b[(d * rows_per_block + k) * piece:(d * rows_per_block + k + 1) * piece]"),
     ("split_shards_misrouted", "                bufs[d][l, p] = shard", "                bufs[num_dst - 1 - d][l, p] = shard"),
+    ("repeats_accepted", "        if t in seen:\n            raise", "        if t in seen and False:\n            raise"),
+    ("reshape_repeats_accepted", "    _reject_repeats([int(s) for s in slots", "    ([int(s) for s in slots"),
+    ("unpack_repeats_accepted", "    _reject_repeats([int(dst_tables[r][j]) for r, j, _ in order",
+     "    ([int(dst_tables[r][j]) for r, j, _ in order"),
+    ("direct_repeats_accepted", "    _reject_repeats([int(d) for t in dst_tables for d in t if 0 <= int(d) < nbd]",
+     "    ([int(d) for t in dst_tables for d in t if 0 <= int(d) < nbd]"),
+    ("kv_first_repeats_accepted", "    _reject_repeats([int(d) for t in dst_tables for d in t if 0 <= int(d) < nb]",
+     "    ([int(d) for t in dst_tables for d in t if 0 <= int(d) < nb]"),
+    ("reshape_repeats_out_of_cache_rejected", "if int(s) >= 0 and int(s) // block_size < num_blocks]", "if int(s) >= 0]"),
+    ("unpack_repeats_out_of_cache_rejected", "order if 0 <= int(dst_tables[r][j]) < nb]", "order]"),
+    ("direct_repeats_out_of_cache_rejected", "for d in t if 0 <= int(d) < nbd]", "for d in t]"),
+    ("kv_first_repeats_out_of_cache_rejected", "for d in t if 0 <= int(d) < nb]", "for d in t]"),
 ]
 
 
