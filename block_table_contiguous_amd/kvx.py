@@ -116,16 +116,41 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
-def _stream(stream) -> Optional[int]:
+_raw_stream = None  # torch's internal raw-handle query, once it has been seen to agree
+
+
+def _public_stream() -> int:
     import torch
 
-    if stream is None:
-        # the raw handle of the current device's current stream, without building a Stream
-        # object (a third of a small call's host time otherwise)
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _current_stream() -> int:
+    """The current device's current stream handle. torch.cuda.current_stream() builds a Stream
+    object per call (a third of a small call's host time), so the binding uses torch's raw
+    handle query instead, but only after checking once that it returns the same handle as the
+    public API; if the query is missing or disagrees, every call uses the public API."""
+    global _raw_stream
+    if _raw_stream is None:
+        import torch
+
         raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-        if raw is not None:
-            return raw(torch._C._cuda_getDevice())
-        stream = torch.cuda.current_stream()
+        dev = getattr(torch._C, "_cuda_getDevice", None)
+        fast = None
+        if raw is not None and dev is not None:
+            fast = lambda: raw(dev())  # noqa: E731
+            try:
+                if fast() != _public_stream():
+                    fast = None
+            except Exception:  # a changed signature: fall back to the public API
+                fast = None
+        _raw_stream = fast or _public_stream
+    return _raw_stream()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return _current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -229,6 +254,8 @@ def kvx_slot_mapping(block_table, req_idx, positions, block_size: int, slot_mapp
     if positions.numel() != T or slot_mapping.numel() != T:
         raise ValueError("kvx: req_idx, positions and slot_mapping need the same length")
     width = block_table.shape[1] if max_blocks_per_req is None else int(max_blocks_per_req)
+    if width > block_table.shape[1]:
+        raise ValueError("kvx: max_blocks_per_req is wider than the block table")
     # a one-row table's row stride is never used (it can be 0 for a broadcast row)
     row_stride = block_table.stride(0) if block_table.shape[0] > 1 else max(block_table.shape[1], width)
     st = _F["kvx_slot_mapping"](_ptr(block_table), block_table.shape[0], width,
@@ -252,6 +279,12 @@ def kvx_reshape_and_cache(key, value, slot_mapping, kv_cache, num_blocks: int, b
     for name, t in (("key", key), ("value", value)):
         if not _rows_contiguous(t):
             raise ValueError(f"kvx: each {name} row must be contiguous")
+    if T and num_blocks > 0:
+        last = ((int(num_blocks) - 1) * int(block_stride_bytes) + (int(block_size) - 1) * int(token_stride_bytes)
+                + int(kv_stride_bytes) + row)
+        room = kv_cache.untyped_storage().nbytes() - kv_cache.storage_offset() * kv_cache.element_size()
+        if last > room:
+            raise ValueError("kvx: num_blocks, block_size and the strides address bytes past the end of kv_cache")
     st = _F["kvx_reshape_and_cache"](_ptr(key), key.stride(0) * e, _ptr(value), value.stride(0) * e,
                                      T, row, _ptr(slot_mapping), _ptr(kv_cache), int(num_blocks),
                                      int(block_size), int(block_stride_bytes), int(token_stride_bytes),
@@ -269,6 +302,10 @@ def kvx_build_xfer_list(src_ids, dst_ids, req_offsets, mode: int, xfers, xfer_co
         if t is not None:
             _want(t, torch.int32, name)
     _want(xfers, torch.int64, "xfers")
+    if req_offsets.numel() < 1:
+        raise ValueError("kvx: req_offsets needs num_reqs + 1 entries")
+    if src_ids is not None and dst_ids is not None and src_ids.numel() != dst_ids.numel():
+        raise ValueError("kvx: src_ids and dst_ids must list the same number of blocks")
     ref = src_ids if src_ids is not None else dst_ids
     total = ref.numel() if ref is not None else 0
     capacity = xfers.numel() // 4

@@ -35,6 +35,40 @@ def host_bytes(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().view(torch.uint8).cpu().numpy().reshape(-1)
 
 
+class HostStage:
+    """Reusable pinned host buffers for streaming large device tensors to the host one at a
+    time (a 1.125 GiB layer at a time for the full-size checks). get() returns a numpy view
+    of the slot's buffer; it stays valid until the next get() on the same slot."""
+
+    def __init__(self):
+        self._bufs = {}
+
+    def get(self, t: torch.Tensor, slot: int = 0) -> np.ndarray:
+        flat = t.detach().contiguous().view(-1).view(torch.uint8)
+        n = flat.numel()
+        b = self._bufs.get(slot)
+        if b is None or b.numel() < n:
+            self._bufs.pop(slot, None)
+            b = torch.empty(max(n, 1), dtype=torch.uint8, pin_memory=True)
+            self._bufs[slot] = b
+        b[:n].copy_(flat, non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+        return b[:n].numpy()
+
+
+def same_bytes(got: np.ndarray, want: np.ndarray) -> bool:
+    """Byte-for-byte equality of two arrays of equal byte size, compared in 64-bit words and
+    256 MiB pieces so a 1 GiB layer needs no 1 GiB temporary."""
+    a = np.ascontiguousarray(got).reshape(-1).view(np.uint8)
+    b = np.ascontiguousarray(want).reshape(-1).view(np.uint8)
+    if a.size != b.size:
+        return False
+    if a.size % 8 == 0:
+        a, b = a.view(np.uint64), b.view(np.uint64)
+    step = 1 << 25
+    return all(np.array_equal(a[i:i + step], b[i:i + step]) for i in range(0, a.size, step))
+
+
 def layers_from_host(arrs, block_bytes):
     """Per-layer uint8 [num_blocks][block_bytes] device tensors (separate allocations)."""
     return [to_dev(np.ascontiguousarray(a).view(np.uint8).reshape(-1, block_bytes)) for a in arrs]

@@ -188,6 +188,30 @@ def test_binding_rejects_undersized_tensors(kvx):
         kvx.kvx_unpack([buf, buf[:100]], bases, 64, 100, 2, x10, c, 10)
     with pytest.raises(TypeError):
         kvx.kvx_pack(bases, 64, 100, x10.int(), c, 10, buf)
+    # run building: both id lists must list the same blocks
+    ro = torch.tensor([0, 10], dtype=torch.int64)
+    ids10, ids9 = torch.zeros(10, dtype=torch.int32), torch.zeros(9, dtype=torch.int32)
+    with pytest.raises(ValueError, match="same number of blocks"):
+        kvx.kvx_build_xfer_list(ids10, ids9, ro, kvx.MODE_DIRECT, x10, c)
+    with pytest.raises(ValueError, match="num_reqs \\+ 1"):
+        kvx.kvx_build_xfer_list(ids10, None, torch.zeros(0, dtype=torch.int64), kvx.MODE_PACK, x10, c)
+    # slot mapping: a width limit past the table's columns would read past each row
+    table = torch.zeros((1, 6), dtype=torch.int32)
+    req, pos = torch.zeros(4, dtype=torch.int32), torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(ValueError, match="wider than the block table"):
+        kvx.kvx_slot_mapping(table, req, pos, 16, torch.zeros(4, dtype=torch.int64), max_blocks_per_req=7)
+    # new-token write: the geometry must stay inside kv_cache's storage
+    cache = torch.zeros((4, 16, 2, 1, 128), dtype=torch.int16)  # 4 blocks of 8 KiB
+    key = torch.zeros((3, 1, 128), dtype=torch.int16)
+    slots = torch.zeros(3, dtype=torch.int64)
+    with pytest.raises(ValueError, match="past the end of kv_cache"):
+        kvx.kvx_reshape_and_cache(key, key, slots, cache, 5, 16, 8192, 512, 256)
+    with pytest.raises(ValueError, match="past the end of kv_cache"):
+        kvx.kvx_reshape_and_cache(key, key, slots, cache[1:], 4, 16, 8192, 512, 256)
+    with pytest.raises(ValueError, match="past the end of kv_cache"):
+        kvx.kvx_reshape_and_cache(key, key, slots, cache, 4, 16, 8192, 528, 256)
+    with pytest.raises(ValueError, match="on the GPU"):  # the exact fit passes the size check
+        kvx.kvx_reshape_and_cache(key, key, slots, cache, 4, 16, 8192, 512, 256)
 
 
 def test_copy_direct_validation(kvx):

@@ -1,20 +1,18 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark times:
 48 layers of [147456][16][K,V][128] bf16 (1.125 GiB each, separate allocations), 8 requests x
 576 blocks, contiguous (runs of 64) and fragmented (geometric run lengths) block tables,
-unpacked into a second 48-layer cache at random ids. Three layers are checked in full against
-the oracle; every layer is checked on sampled blocks the oracle places one by one."""
+unpacked into a second 48-layer cache at random ids. Every layer is streamed to the host and
+compared whole, byte for byte, with the oracle's output for that layer: the send buffer's
+slice and the entire destination cache (listed blocks and the untouched rest)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import workloads as W
-from gpu_util import DEV, Transfer, check_runs_equal, host_bytes, kvx, log, to_dev
+from gpu_util import DEV, HostStage, Transfer, check_runs_equal, kvx, log, same_bytes, to_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.big]
-
-FULL_LAYERS = (0, 23, 47)
-SAMPLES = 384
 
 
 @pytest.fixture(scope="module")
@@ -35,62 +33,61 @@ def pages_caches():
     torch.cuda.empty_cache()
 
 
-def _check_transfer(case, src, dst):
+@pytest.fixture(scope="module")
+def stage():
+    st = HostStage()
+    yield st
+    st._bufs.clear()
+
+
+def _progress(what, l, L):
+    if l % 8 == 7 or l == L - 1:
+        log(f"{what}: layers 0..{l} identical")
+
+
+def _check_transfer(case, src, dst, stage):
     for t in dst:
         W.fill_device_byte_(t)
     tr = Transfer(case, src, dst)
     tr.run()
     log(f"{case.name}: transfer done, checking")
-    _verify(case, tr)
+    _verify(case, tr, stage)
 
 
-def _verify(case, tr):
-    """The run lists, the send buffer and the destination caches against the oracle: three
-    layers in full, every layer on sampled blocks, and untouched blocks still the fill byte."""
+def _verify(case, tr, stage):
+    """The run lists, then every layer: its slice of the send buffer against the oracle's pack
+    of the host copy of that layer, and the whole destination layer against the oracle's
+    unpack of that buffer into a cache holding the fill byte (as the device cache did)."""
     spec, src, dst = case.src_spec, tr.src, tr.dst
     assert tr.err_bits() == 0
     check_runs_equal(tr.K, tr.xp, tr.cp, O.xfer_list(case.src_tables, case.dst_tables, O.MODE_PACK))
     check_runs_equal(tr.K, tr.xu, tr.cu, O.xfer_list(case.src_tables, case.dst_tables, O.MODE_UNPACK))
-    N, BB = tr.N, tr.BB
-    buf = tr.buf.view(spec.num_layers, N, BB)
-    for l in FULL_LAYERS:
-        src_l = host_bytes(src[l]).reshape(spec.num_blocks, BB)
-        exp_buf, e1 = O.pack([src_l], case.src_tables)
-        assert np.array_equal(host_bytes(buf[l]).reshape(N, BB), exp_buf[0]), f"pack layer {l}"
-        before = np.full((spec.num_blocks, BB), W.FILL_BYTE, np.uint8)
+    L, N, BB, nb = spec.num_layers, tr.N, tr.BB, spec.num_blocks
+    buf = tr.buf.view(L, N, BB)
+    before = np.full((nb, BB), W.FILL_BYTE, np.uint8)
+    for l in range(L):
+        exp_buf, e1 = O.pack([stage.get(src[l], 0).reshape(nb, BB)], case.src_tables)
+        assert same_bytes(stage.get(buf[l], 1), exp_buf), f"pack layer {l}"
         exp_dst, e2 = O.unpack([exp_buf], [before], case.dst_tables)
-        assert np.array_equal(host_bytes(dst[l]).reshape(spec.num_blocks, BB), exp_dst[0]), f"unpack layer {l}"
+        assert same_bytes(stage.get(dst[l], 2), exp_dst[0]), f"unpack layer {l}"
         assert e1 == e2 == 0
-        log(f"{case.name}: layer {l} identical")
-    order = O.buffer_order(case.src_tables)
-    rng = np.random.default_rng(case.seed)
-    listed = set(int(x) for x in np.concatenate(case.dst_tables))
-    for _ in range(SAMPLES):
-        l = int(rng.integers(spec.num_layers))
-        r, j, p = order[int(rng.integers(N))]
-        s_id, d_id = int(case.src_tables[r][j]), int(case.dst_tables[r][j])
-        want = host_bytes(src[l][s_id])
-        assert np.array_equal(host_bytes(buf[l, p]), want), (l, p)
-        assert np.array_equal(host_bytes(dst[l][d_id]), want), (l, d_id)
-        free = int(rng.integers(spec.num_blocks))
-        if free not in listed:
-            assert np.all(host_bytes(dst[l][free]) == W.FILL_BYTE), (l, free)
-    log(f"{case.name}: {SAMPLES} sampled blocks identical")
+        _progress(case.name, l, L)
 
 
-def test_pages_contiguous_full(pages_caches):
+def test_pages_contiguous_full(pages_caches, stage):
     spec, src, dst = pages_caches
-    _check_transfer(W.pages_contiguous(), src, dst)
+    _check_transfer(W.pages_contiguous(), src, dst, stage)
 
 
-def test_pages_fragmented_full(pages_caches):
+def test_pages_fragmented_full(pages_caches, stage):
     spec, src, dst = pages_caches
-    _check_transfer(W.pages_fragmented(), src, dst)
+    _check_transfer(W.pages_fragmented(), src, dst, stage)
 
 
-def test_pages_contiguous_kv_first_full(pages_caches):
+def test_pages_contiguous_kv_first_full(pages_caches, stage):
     """The same 48 allocations viewed as kv-first caches (K plane, V plane) of 147456 blocks
-    with 4 KiB segments: pack and unpack through the kv-first entry points."""
+    with 4 KiB segments: pack and unpack through the kv-first entry points, every layer
+    compared whole with the oracle's kv-first pack and unpack."""
     spec, src, dst = pages_caches
     case = W.pages_contiguous()
     K = kvx()
@@ -111,41 +108,22 @@ def test_pages_contiguous_kv_first_full(pages_caches):
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     bufv = buf.view(L, 2 * N, seg)
-    for l in FULL_LAYERS:
-        src_l = host_bytes(src[l]).reshape(2, nb, seg)
-        exp_buf, e1 = O.pack_kv_first([src_l], case.src_tables)
-        assert np.array_equal(host_bytes(bufv[l]).reshape(2 * N, seg), exp_buf[0]), f"kv-first pack layer {l}"
-        before = np.full((2, nb, seg), W.FILL_BYTE, np.uint8)
+    before = np.full((2, nb, seg), W.FILL_BYTE, np.uint8)
+    for l in range(L):
+        exp_buf, e1 = O.pack_kv_first([stage.get(src[l], 0).reshape(2, nb, seg)], case.src_tables)
+        assert same_bytes(stage.get(bufv[l], 1), exp_buf), f"kv-first pack layer {l}"
         exp_dst, e2 = O.unpack_kv_first(exp_buf, [before], case.dst_tables)
-        assert np.array_equal(host_bytes(dst[l]).reshape(2, nb, seg), exp_dst[0]), f"kv-first unpack layer {l}"
+        assert same_bytes(stage.get(dst[l], 2), exp_dst[0]), f"kv-first unpack layer {l}"
         assert e1 == e2 == 0
-        log(f"kv-first: layer {l} identical")
-    # where each (plane, source block) lands in a layer's buffer, as the oracle places it:
-    # pack a tag cache whose segment (kv, b) holds the number kv*nb + b
-    tags = (np.arange(2 * nb, dtype=np.int64).reshape(2, nb, 1)).view(np.uint8)
-    tag_buf, _ = O.pack_kv_first([tags], case.src_tables)
-    where = tag_buf[0].copy().view(np.int64).reshape(-1)  # segment g -> kv*nb + source id
-    pos_of_src = {int(v): g for g, v in enumerate(where)}
-    src_to_dst = {int(s): int(d) for s, d in zip(np.concatenate(case.src_tables), np.concatenate(case.dst_tables))}
-    rng = np.random.default_rng(7)
-    for _ in range(SAMPLES):
-        l = int(rng.integers(L))
-        g = int(rng.integers(2 * N))
-        kv, s_id = divmod(int(where[g]), nb)
-        d_id = src_to_dst[s_id]
-        want = host_bytes(src[l].view(2, nb, seg)[kv, s_id])
-        assert pos_of_src[kv * nb + s_id] == g
-        assert np.array_equal(host_bytes(bufv[l, g]), want), (l, g)
-        assert np.array_equal(host_bytes(dst[l].view(2, nb, seg)[kv, d_id]), want), (l, g, d_id)
-    log(f"kv-first: {SAMPLES} sampled segments identical")
+        _progress("kv-first", l, L)
 
 
-def test_step_new_token_write_full(pages_caches):
-    """The rest of the benchmark's step at full size: after the contiguous transfer, the
-    receiver's slot mapping for each request's last prompt token (recomputed locally) and the
-    per-layer new-token write of its 256-byte K and V rows into all 48 destination layers, one
-    launch per layer as in the step. Every block that receives a new row is compared with the
-    oracle: the block as the transfer left it (the source block), then the oracle's write."""
+def test_step_new_token_write_full(pages_caches, stage):
+    """The benchmark's whole step at full size: the contiguous transfer, then the receiver's
+    slot mapping for each request's last prompt token (recomputed locally) and the per-layer
+    new-token write of its 256-byte K and V rows into all 48 destination layers, one launch
+    per layer as in the step. Every destination layer is compared whole with the oracle's
+    pack, unpack and new-token write of that layer."""
     spec, src, dst = pages_caches
     case = W.pages_contiguous()
     for t in dst:
@@ -153,7 +131,7 @@ def test_step_new_token_write_full(pages_caches):
     tr = Transfer(case, src, dst)
     tr.run()
     K = tr.K
-    L, nb, bs, row = spec.num_layers, spec.num_blocks, spec.block_size, spec.row_bytes
+    L, nb, bs, row, BB = spec.num_layers, spec.num_blocks, spec.block_size, spec.row_bytes, spec.block_bytes
     R = len(case.dst_tables)
     table_h = W.pad_table(case.dst_tables, max(len(t) for t in case.dst_tables))
     req_h = np.arange(R, dtype=np.int32)
@@ -173,25 +151,21 @@ def test_step_new_token_write_full(pages_caches):
     assert int(err.item()) == 0 and tr.err_bits() == 0
     exp_slots, e = O.slot_mapping(table_h, req_h, pos_h, bs)
     assert e == 0 and np.array_equal(slots.cpu().numpy(), exp_slots)
-    # the written blocks, gathered into a small cache: block i of it is destination block blocks[i]
-    blocks = sorted(set(int(s) // bs for s in exp_slots))
-    where = {b: i for i, b in enumerate(blocks)}
-    mini_slots = np.array([where[int(s) // bs] * bs + int(s) % bs for s in exp_slots], np.int64)
-    dst_to_src = {int(d): int(s_) for s_, d in zip(np.concatenate(case.src_tables), np.concatenate(case.dst_tables))}
+    before = np.full((nb, BB), W.FILL_BYTE, np.uint8)
     for l in range(L):
-        before = np.stack([host_bytes(src[l][dst_to_src[b]]) for b in blocks])
-        exp, e = O.reshape_and_cache(before, new_k[l], new_v[l], mini_slots, len(blocks), bs, bst, tst, kst)
-        assert e == 0
-        got = np.stack([host_bytes(dst[l][b]) for b in blocks]).reshape(-1)
-        assert np.array_equal(got, exp), f"layer {l}"
-    log(f"new-token write: {R} tokens x {L} layers identical")
+        exp_buf, e1 = O.pack([stage.get(src[l], 0).reshape(nb, BB)], case.src_tables)
+        moved, e2 = O.unpack([exp_buf], [before], case.dst_tables)
+        exp, e3 = O.reshape_and_cache(moved[0], new_k[l], new_v[l], exp_slots, nb, bs, bst, tst, kst)
+        assert e1 == e2 == e3 == 0
+        assert same_bytes(stage.get(dst[l], 2), exp), f"layer {l}"
+        _progress("step with new-token writes", l, L)
 
 
-def test_layer_pipelined_transfer_full(pages_caches):
+def test_layer_pipelined_transfer_full(pages_caches, stage):
     """The contiguous transfer layer by layer at full size: per layer, a bf16 product on a
     forward stream, then on a copy stream that layer's pack and a signal add, and on a
     consumer stream the signal wait and that layer's unpack. Checked like the one-launch
-    transfer."""
+    transfer, every layer whole."""
     spec, src, dst = pages_caches
     case = W.pages_contiguous()
     for t in dst:
@@ -220,13 +194,13 @@ def test_layer_pipelined_transfer_full(pages_caches):
     torch.cuda.synchronize()
     assert int(werr.item()) == 0 and int(counter.item()) == L
     log("layer-pipelined transfer done, checking")
-    _verify(case, tr)
+    _verify(case, tr, stage)
 
 
-def test_pages_contiguous_direct_full(pages_caches):
+def test_pages_contiguous_direct_full(pages_caches, stage):
     """The contiguous transfer at full size with no send buffer: runs built in direct mode,
     every listed block of the 48 layers copied from the source caches into the destination
-    caches. Three layers checked in full against the oracle, all layers on sampled blocks."""
+    caches. Every destination layer compared whole with the oracle's direct copy."""
     spec, src, dst = pages_caches
     case = W.pages_contiguous()
     K = kvx()
@@ -242,23 +216,16 @@ def test_pages_contiguous_direct_full(pages_caches):
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     check_runs_equal(K, x, c, O.xfer_list(case.src_tables, case.dst_tables, O.MODE_DIRECT))
-    for l in FULL_LAYERS:
-        before = np.full((nb, BB), W.FILL_BYTE, np.uint8)
-        exp, e = O.copy_direct([host_bytes(src[l]).reshape(nb, BB)], [before], case.src_tables,
+    before = np.full((nb, BB), W.FILL_BYTE, np.uint8)
+    for l in range(L):
+        exp, e = O.copy_direct([stage.get(src[l], 0).reshape(nb, BB)], [before], case.src_tables,
                                case.dst_tables)
         assert e == 0
-        assert np.array_equal(host_bytes(dst[l]).reshape(nb, BB), exp[0]), f"direct layer {l}"
-        log(f"direct: layer {l} identical")
-    rng = np.random.default_rng(case.seed + 1)
-    flat_s, flat_d = np.concatenate(case.src_tables), np.concatenate(case.dst_tables)
-    for _ in range(SAMPLES):
-        l = int(rng.integers(L))
-        i = int(rng.integers(N))
-        assert np.array_equal(host_bytes(dst[l][int(flat_d[i])]), host_bytes(src[l][int(flat_s[i])])), (l, i)
-    log(f"direct: {SAMPLES} sampled blocks identical")
+        assert same_bytes(stage.get(dst[l], 2), exp[0]), f"direct layer {l}"
+        _progress("direct", l, L)
 
 
-def test_run_lists_past_the_workgroup_cap():
+def test_run_lists_past_the_workgroup_cap(stage):
     """1.18M blocks of 16 bytes in 300 requests: more tiles than the run builder's workgroups,
     so each workgroup walks several sub-tiles. Run lists in both modes and the transfer's
     bytes against the oracle."""
@@ -280,5 +247,5 @@ def test_run_lists_past_the_workgroup_cap():
     exp_buf, e1 = O.pack(case.src_caches, case.src_tables)
     exp_dst, e2 = O.unpack([exp_buf], case.dst_caches, case.dst_tables)
     assert e1 == e2 == 0
-    assert np.array_equal(host_bytes(tr.buf)[: exp_buf.nbytes], exp_buf.reshape(-1))
-    assert np.array_equal(host_bytes(dst[0]), exp_dst[0].reshape(-1))
+    assert same_bytes(stage.get(tr.buf, 1)[: exp_buf.nbytes], exp_buf)
+    assert same_bytes(stage.get(dst[0], 2), exp_dst[0])
