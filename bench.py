@@ -14,7 +14,8 @@ One step = one pass of the whole hot path over that batch:
 `value` = algorithmic bytes of the step (read + write of every moved byte) / step time.
 "roofline" is the slower of pack and unpack in the timed steps (HIP events on their stream).
 
-Under "ops", each after evicting the Infinity Cache: the same caches as kv-first views, the
+Under "ops", each after evicting the Infinity Cache: the same caches under the other
+block-table shape (fragmented tables for the contiguous headline), as kv-first views, the
 direct cache-to-cache copy, the layer-pipelined pack beside a GEMM forward stand-in, the
 asymmetric-TP head merge and split (32 layers, 64 KiB blocks), and the 32-request decode
 slot mapping and new-token write (rows of 8 heads, 2 KiB, and of 1 head, 256 B). "cpu_baseline" is the CPU oracle on the whole step.
@@ -22,7 +23,7 @@ slot mapping and new-token write (rows of 8 heads, 2 KiB, and of 1 head, 256 B).
 stays the eager rate: a graph is fixed to one transfer size).
 
     python bench.py [--steps K] [--warmup W] [--workload contiguous|fragmented]
-                    [--no-cpu-baseline] [--no-ops] [--no-graph] [--copy-calib]
+                    [--no-cpu-baseline] [--no-ops] [--no-pipeline] [--no-graph] [--copy-calib]
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -65,6 +66,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ops", action="store_true")
     ap.add_argument("--op-reps", type=int, default=10)
+    ap.add_argument("--no-pipeline", action="store_true",
+                    help="skip the layer-pipelined pack beside the forward stand-in (ops.layer_pipeline)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the step replayed from a captured HIP graph (graph_ms_per_step)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -310,8 +313,12 @@ def main():
             "vs_pack_plus_unpack": round((out_ops["pack"]["flushed_median_ms"] + out_ops["unpack"]["flushed_median_ms"]) / med, 3)}
         torch.cuda.synchronize()
         assert int(err.item()) == 0, "device error flag raised"
-        out_ops["layer_pipeline"] = layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err,
-                                                   max(3, args.op_reps // 2))
+        other = W.pages_fragmented() if case.name == "contiguous" else W.pages_contiguous()
+        out_ops[other.name] = other_tables(torch, K, dev, flush, args.op_reps, other, src_bases, dst_bases,
+                                           buf, L, nb, BB, err)
+        if not args.no_pipeline:
+            out_ops["layer_pipeline"] = layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err,
+                                                       max(3, args.op_reps // 2))
         out_ops.update(other_workloads(torch, np, W, K, dev, flush, args.op_reps))
 
     cpu = None
@@ -347,6 +354,41 @@ def main():
         "kernel_source_sha256_16": kernel_source_hash(),
     }
     print(json.dumps(result), flush=True)
+
+
+def other_tables(torch, K, dev, flush, reps, case, src_bases, dst_bases, buf, L, nb, BB, err):
+    """The same 48-layer caches under the other block-table shape (for the contiguous headline:
+    the fragmented tables, geometric(0.5) run lengths, about 2,300 pack runs against 72): both
+    run-list builds, pack and unpack, each timed after evicting the Infinity Cache."""
+    N = case.total_blocks
+    sid, ro = K.flatten_tables(case.src_tables, dev)
+    did, _ = K.flatten_tables(case.dst_tables, dev)
+    xp, cp = K.new_xfer_list(N, dev)
+    xu, cu = K.new_xfer_list(N, dev)
+    nbytes = 2 * L * N * BB
+    out = {"workload": f"{case.name}: the same {L} caches, 8 requests x 576 blocks, "
+                       + ("geometric(0.5) run lengths" if case.name == "fragmented" else "runs of 64"),
+           "bytes": nbytes}
+    for name, fn in (("build_pack", lambda: K.kvx_build_xfer_list(sid, None, ro, K.MODE_PACK, xp, cp, err)),
+                     ("build_unpack", lambda: K.kvx_build_xfer_list(None, did, ro, K.MODE_UNPACK, xu, cu, err))):
+        med, mn = time_op(torch, fn, reps, flush)
+        out[name] = {"median_ms": round(med, 5)}
+    torch.cuda.synchronize()
+    runs = {"pack": int(cp.item()), "unpack": int(cu.item())}
+    out["build_pack"]["runs"], out["build_unpack"]["runs"] = runs["pack"], runs["unpack"]
+    for name, fn in (("pack", lambda: K.kvx_pack(src_bases, BB, nb, xp, cp, N, buf, err)),
+                     ("unpack", lambda: K.kvx_unpack([buf], dst_bases, BB, nb, 1, xu, cu, N, err))):
+        med, mn = time_op(torch, fn, reps, flush)
+        out[name] = {"median_ms": round(med, 5), "min_ms": round(mn, 5),
+                     "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1),
+                     "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "runs": runs[name] * L, "ns_per_run": round(med * 1e6 / max(runs[name] * L, 1), 2),
+                     "traffic": traffic_from_counters(f"{name}_{case.name}", nbytes)}
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, "device error flag raised"
+    log(f"{case.name} tables: pack {out['pack']['GB/s']} GB/s, unpack {out['unpack']['GB/s']} GB/s, "
+        f"{runs['pack']} / {runs['unpack']} runs")
+    return out
 
 
 def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, reps):
@@ -473,6 +515,18 @@ def other_workloads(torch, np, W, K, dev, flush, reps):
         "bytes": nbytes, "median_ms": round(med, 4), "min_ms": round(mn, 4),
         "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "traffic": traffic_from_counters("merge_asym_tp", nbytes)}
+    # the same destination blocks and bytes from one full-head buffer: a plain unpack, the
+    # merge's own shape without the head interleave (its cost against the merge's)
+    one = torch.empty((L, N, BB), dtype=torch.uint8, device=dev)
+    W.fill_device_random_(one, case.seed * 10 + 7)
+    med, mn = time_op(torch, lambda: K.kvx_unpack([one], bases, BB, nb, 1, x, c, N), reps, flush)
+    out["unpack_asym_tp_shape"] = {
+        "workload": "one buffer of all 8 heads, 32 layers x 16 requests x 256 blocks -> the same [8192][16][K,V][8][128] "
+                    "bf16 caches and destination ids as the merge",
+        "bytes": nbytes, "median_ms": round(med, 4), "min_ms": round(mn, 4),
+        "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "traffic": traffic_from_counters("unpack_asym_tp_shape", nbytes)}
+    del one
     # the sender side of the same shapes: full-head caches split into 2 head shards
     xs, cs = K.new_xfer_list(N, dev)
     K.kvx_build_xfer_list(ids, None, ro, K.MODE_PACK, xs, cs)

@@ -69,6 +69,22 @@ def same_bytes(got: np.ndarray, want: np.ndarray) -> bool:
     return all(np.array_equal(a[i:i + step], b[i:i + step]) for i in range(0, a.size, step))
 
 
+def reshape_and_cache_raw(K, key, value, slots, cache, num_blocks, block_size, block_stride,
+                          token_stride, kv_stride, err):
+    """The new-token write through the C entry point itself, skipping the binding's geometry
+    check. For geometries whose blocks overlap on purpose (2^30-slot blocks 64 KiB apart, to
+    reach slots past 2^31 without a 512 GiB cache): the binding bounds the addressed bytes by
+    the geometry, while these tests keep every slot inside the allocation, which is what the
+    C entry point asks of its caller."""
+    T = slots.numel()
+    row = key.numel() // T * key.element_size()
+    st = K._F["kvx_reshape_and_cache"](key.data_ptr(), row, value.data_ptr(), row, T, row, slots.data_ptr(),
+                                       cache.data_ptr(), int(num_blocks), int(block_size), int(block_stride),
+                                       int(token_stride), int(kv_stride), err.data_ptr(),
+                                       torch.cuda.current_stream().cuda_stream)
+    assert st == K.KVX_SUCCESS, st
+
+
 def layers_from_host(arrs, block_bytes):
     """Per-layer uint8 [num_blocks][block_bytes] device tensors (separate allocations)."""
     return [to_dev(np.ascontiguousarray(a).view(np.uint8).reshape(-1, block_bytes)) for a in arrs]

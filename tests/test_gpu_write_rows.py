@@ -9,7 +9,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_util import DEV, host_bytes, kvx, log, to_dev
+from gpu_util import DEV, host_bytes, kvx, log, reshape_and_cache_raw, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -101,7 +101,7 @@ def test_vector_kernel_slots_past_32_bits(bs):
     cache_h = np.full(nb * bst // 2, W.SENTINEL16, np.uint16)
     cache = to_dev(cache_h)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
-    K.kvx_reshape_and_cache(to_dev(key), to_dev(val), to_dev(slots), cache, nb, bs, bst, tst, kst, err)
+    reshape_and_cache_raw(K, to_dev(key), to_dev(val), to_dev(slots), cache, nb, bs, bst, tst, kst, err)
     torch.cuda.synchronize()
     exp, e = O.reshape_and_cache(cache_h, key, val, slots, nb, bs, bst, tst, kst)
     assert np.array_equal(host_bytes(cache), exp)
