@@ -31,7 +31,7 @@ const char* kvx_status_string(kvx_status status) {
   return "kvx: unknown status";
 }
 
-int32_t kvx_abi_version(void) { return 3; }
+int32_t kvx_abi_version(void) { return 4; }
 
 kvx_status kvx_slot_mapping(const int32_t* block_table, int64_t num_reqs,
                             int64_t max_blocks_per_req, int64_t bt_row_stride,
@@ -173,6 +173,55 @@ kvx_status kvx_pack_split(void* const* layer_bases, int32_t num_layers, int64_t 
   return from_hip(kvx::launch_shards(true, send_bufs, num_dst, layer_bases, num_layers, block_bytes,
                                      num_cache_blocks, rows_per_block, xfers, xfer_count,
                                      total_blocks, err_flag, stream));
+}
+
+static kvx_status signal_checks(uint64_t* counter, uint32_t* arrivals) {
+  if (!counter || !arrivals) return KVX_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)counter & 7u) != 0 || ((uintptr_t)arrivals & 127u) != 0) return KVX_ERR_MISALIGNED;
+  return KVX_SUCCESS;
+}
+
+kvx_status kvx_pack_signal(void* const* layer_bases, int32_t num_layers, int64_t block_bytes,
+                           int64_t num_cache_blocks, const kvx_xfer* xfers,
+                           const int64_t* xfer_count, int64_t total_blocks, void* send_buf,
+                           uint64_t* counter, uint64_t delta, uint32_t* arrivals,
+                           int32_t* err_flag, hipStream_t stream) {
+  const kvx_status sc = signal_checks(counter, arrivals);
+  if (sc != KVX_SUCCESS) return sc;
+  if (num_layers < 0 || block_bytes <= 0 || num_cache_blocks < 0 || total_blocks < 0 ||
+      total_blocks > kMaxBlocks)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (num_layers == 0 || total_blocks == 0)  // nothing to copy: the signal still goes out
+    return from_hip(kvx::launch_signal_add(counter, delta, stream));
+  if (!layer_bases || !xfers || !xfer_count || !send_buf) return KVX_ERR_INVALID_ARGUMENT;
+  if (!mult16(block_bytes) || !aligned16(send_buf)) return KVX_ERR_MISALIGNED;
+  const kvx::SignalSpec sig = {counter, delta, arrivals};
+  return from_hip(kvx::launch_copy_runs(kvx::kDirToBuffer, layer_bases, nullptr, num_layers,
+                                        block_bytes, num_cache_blocks, 0, xfers, xfer_count,
+                                        total_blocks, send_buf, err_flag, stream, &sig));
+}
+
+kvx_status kvx_copy_direct_signal(void* const* src_layer_bases, void* const* dst_layer_bases,
+                                  int32_t num_layers, int64_t block_bytes, int64_t src_num_blocks,
+                                  int64_t dst_num_blocks, const kvx_xfer* xfers,
+                                  const int64_t* xfer_count, int64_t total_blocks,
+                                  uint64_t* counter, uint64_t delta, uint32_t* arrivals,
+                                  int32_t* err_flag, hipStream_t stream) {
+  const kvx_status sc = signal_checks(counter, arrivals);
+  if (sc != KVX_SUCCESS) return sc;
+  if (num_layers < 0 || block_bytes <= 0 || src_num_blocks < 0 || dst_num_blocks < 0 ||
+      total_blocks < 0 || total_blocks > kMaxBlocks)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (num_layers == 0 || total_blocks == 0)
+    return from_hip(kvx::launch_signal_add(counter, delta, stream));
+  if (!src_layer_bases || !dst_layer_bases || !xfers || !xfer_count || src_num_blocks == 0)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (!mult16(block_bytes)) return KVX_ERR_MISALIGNED;
+  const kvx::SignalSpec sig = {counter, delta, arrivals};
+  return from_hip(kvx::launch_copy_runs(kvx::kDirDirect, src_layer_bases, dst_layer_bases,
+                                        num_layers, block_bytes, src_num_blocks, dst_num_blocks,
+                                        xfers, xfer_count, total_blocks, nullptr, err_flag, stream,
+                                        &sig));
 }
 
 static kvx_status kv_first_checks(void* const* layer_bases, int32_t num_layers,

@@ -118,6 +118,25 @@ __device__ __forceinline__ void store16(char* p, u32x4 v) {
   else *g = v;
 }
 
+// Cache-policy bits of buffer instructions on gfx950: sc1 makes a store device-coherent
+// (written through to the device's coherence point rather than held dirty in one XCD's L2),
+// nt marks it non-temporal. Word 3 of a raw buffer resource.
+constexpr int kCpolNt = 2, kCpolSc1 = 16;
+constexpr int kRsrcWord3 = 0x00020000;
+
+// A wavefront's 16-byte store at base + lane_off, base uniform across the wavefront. With
+// DEVICE the store is device-coherent: once it is acknowledged (vmcnt) every XCD can read it,
+// with no L2 write-back. Otherwise a plain global store with the NT policy.
+template <bool NT, bool DEVICE>
+__device__ __forceinline__ void store16_at(char* base, int64_t lane_off, u32x4 v) {
+  if constexpr (DEVICE) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, kWaveBytes, kRsrcWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)lane_off, 0, NT ? (kCpolSc1 | kCpolNt) : kCpolSc1);
+  } else {
+    store16<NT>(base + lane_off, v);
+  }
+}
+
 __device__ __forceinline__ int64_t uniform(int64_t v) {
   const int32_t lo = __builtin_amdgcn_readfirstlane((int32_t)(v & 0xffffffff));
   const int32_t hi = __builtin_amdgcn_readfirstlane((int32_t)(v >> 32));
@@ -140,7 +159,7 @@ __device__ __forceinline__ int64_t xcd_slice_order(int64_t b, int64_t n) {
 // One wavefront copies nbytes (a multiple of 16) from src to dst. Batch j of K covers
 // bytes [base + j KiB, base + (j+1) KiB): each instruction is one coalesced 1 KiB access,
 // and a lane issues all K loads of a batch before its K stores.
-template <int K, bool NTL, bool NTS>
+template <int K, bool NTL, bool NTS, bool DEVICE = false>
 __device__ __forceinline__ void wave_copy(const char* __restrict__ src, char* __restrict__ dst,
                                           int64_t nbytes, int lane) {
   constexpr int64_t kBatch = (int64_t)K * kWaveBytes;
@@ -151,7 +170,7 @@ __device__ __forceinline__ void wave_copy(const char* __restrict__ src, char* __
 #pragma unroll
     for (int j = 0; j < K; ++j) v[j] = load16<NTL>(src + base + j * kWaveBytes + lo);
 #pragma unroll
-    for (int j = 0; j < K; ++j) store16<NTS>(dst + base + j * kWaveBytes + lo, v[j]);
+    for (int j = 0; j < K; ++j) store16_at<NTS, DEVICE>(dst + base + j * kWaveBytes, lo, v[j]);
   }
   if (base < nbytes) {
     u32x4 v[K];
@@ -163,7 +182,7 @@ __device__ __forceinline__ void wave_copy(const char* __restrict__ src, char* __
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const int64_t o = base + j * kWaveBytes + lo;
-      if (o < nbytes) store16<NTS>(dst + o, v[j]);
+      if (o < nbytes) store16_at<NTS, DEVICE>(dst + base + j * kWaveBytes, lo, v[j]);
     }
   }
 }
@@ -751,7 +770,48 @@ struct RunCopyArgs {
   int64_t num_wgs;
   int32_t num_layers;
   int32_t xcd_remap;
+  // completion signal folded into the launch (pack and direct only; null otherwise)
+  uint64_t* signal;
+  uint64_t signal_delta;
+  uint32_t* arrivals;  // workgroups of the launch that have finished; every launch leaves it 0
 };
+
+// The completion signal inside a copy launch ("5. flagcx connector design & dev & test",
+// §1.2: the sender's last write of a batch carries the signal that the receiver counts).
+// In a signalling launch every data store is device-coherent (store16_at<., true>), so a
+// store that has been acknowledged is at the device's coherence point and no XCD holds it
+// dirty in its L2. Each wavefront waits for its acknowledgements and the workgroup meets at a
+// barrier; then one thread counts the workgroup. Counting goes through kArrivalGroups group
+// counters (workgroup b counts in group b % kArrivalGroups), each on its own 128-byte line,
+// and one top counter: the last workgroup of a group resets its group counter and counts the
+// group at the top; the last group resets the top counter and adds `delta` to the signal
+// counter. Every workgroup's bytes were acknowledged before it counted itself, so whoever
+// reads the new signal count reads every byte of the launch, and all counters are back at 0
+// for the next launch. Spreading the counts over 16 lines keeps a 2304-workgroup launch from
+// queueing on one address; no workgroup writes back or invalidates an L2 (an agent-scope
+// release per workgroup writes the XCD's whole L2 back each time). The counter words are
+// touched only by vector atomics and stores from one lane, never through the scalar cache.
+constexpr uint32_t kArrivalGroups = 16;
+constexpr uint32_t kArrivalStride = 32;  // 32-bit words between counters: one 128-byte line
+
+__device__ __forceinline__ void arrive_and_signal(uint32_t* arrivals, uint64_t* counter, uint64_t delta) {
+  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's stores are acknowledged
+  __syncthreads();                // and so are those of the other wavefronts
+  if (threadIdx.x == 0) {
+    const uint32_t G = gridDim.x, b = blockIdx.x;
+    const uint32_t groups = G < kArrivalGroups ? G : kArrivalGroups;
+    const uint32_t g = b % kArrivalGroups;
+    const uint32_t members = (G - g + kArrivalGroups - 1) / kArrivalGroups;
+    uint32_t* gc = arrivals + (1 + g) * kArrivalStride;
+    if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == members) {
+      __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__hip_atomic_fetch_add(arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == groups) {
+        __hip_atomic_store(arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(counter, delta, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+  }
+}
 
 
 // Work split: wavefront w owns layer l = w / waves_per_layer and buffer positions
@@ -759,8 +819,8 @@ struct RunCopyArgs {
 // same number of bytes whatever the run lengths. It finds the run holding its first
 // position, then walks the runs overlapping its range; each overlap is one contiguous copy
 // on both sides (run blocks are consecutive in the cache and in the buffer).
-template <int DIR, bool NTL, bool NTS>
-__global__ __launch_bounds__(kCopyThreads) void copy_runs_kernel(RunCopyArgs a) {
+template <int DIR, bool NTL, bool NTS, bool DEVICE>
+__device__ __forceinline__ void copy_runs_body(const RunCopyArgs& a) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t wg = blockIdx.x;
   if (a.xcd_remap) wg = xcd_slice_order(wg, a.num_wgs);
@@ -805,11 +865,17 @@ __global__ __launch_bounds__(kCopyThreads) void copy_runs_kernel(RunCopyArgs a) 
     if (nlo >= nhi) continue;
     const int64_t bytes = (nhi - nlo) * BB;
     char* cptr = cache + (sid + (nlo - lo)) * BB;
-    if (DIR == kToBuffer) wave_copy<kCopyBatch, NTL, NTS>(cptr, buf + nlo * BB, bytes, lane);
-    else if (DIR == kFromBuffer) wave_copy<kCopyBatch, NTL, NTS>(buf + nlo * BB, cptr, bytes, lane);
-    else wave_copy<kCopyBatch, NTL, NTS>(cptr, dcache + (did + (nlo - lo)) * BB, bytes, lane);
+    if (DIR == kToBuffer) wave_copy<kCopyBatch, NTL, NTS, DEVICE>(cptr, buf + nlo * BB, bytes, lane);
+    else if (DIR == kFromBuffer) wave_copy<kCopyBatch, NTL, NTS, DEVICE>(buf + nlo * BB, cptr, bytes, lane);
+    else wave_copy<kCopyBatch, NTL, NTS, DEVICE>(cptr, dcache + (did + (nlo - lo)) * BB, bytes, lane);
   }
   if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_BLOCK_RANGE);
+}
+
+template <int DIR, bool NTL, bool NTS, bool SIGNAL>
+__global__ __launch_bounds__(kCopyThreads) void copy_runs_kernel(RunCopyArgs a) {
+  copy_runs_body<DIR, NTL, NTS, SIGNAL>(a);
+  if constexpr (SIGNAL) arrive_and_signal(a.arrivals, a.signal, a.signal_delta);
 }
 
 // --------------------------------------------------------------------------------------
@@ -933,8 +999,8 @@ __global__ __launch_bounds__(kCopyThreads) void shard_runs_kernel(ShardArgs a) {
 // then the wavefront issues all its loads, then all its stores, and exits. On this
 // architecture stores count in vmcnt, so a wavefront with a second batch would wait for its
 // first batch's store acknowledgements; one batch per wavefront never does.
-template <int DIR, bool NTL, bool NTS, int K>
-__global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(RunCopyArgs a) {
+template <int DIR, bool NTL, bool NTS, int K, bool DEVICE>
+__device__ __forceinline__ void copy_slots_body(const RunCopyArgs& a) {
   const int lane = threadIdx.x & (kWave - 1);
   int64_t wg = blockIdx.x;
   if (a.xcd_remap) wg = xcd_slice_order(wg, a.num_wgs);
@@ -1000,8 +1066,14 @@ __global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(RunCopyArgs a)
   for (int j = 0; j < K; ++j) v[j] = load16<NTL>(sp[j] + lane * kVec);
 #pragma unroll
   for (int j = 0; j < K; ++j)
-    if (on[j]) store16<NTS>(dp[j] + lane * kVec, v[j]);
+    if (on[j]) store16_at<NTS, DEVICE>(dp[j], lane * kVec, v[j]);
   if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_BLOCK_RANGE);
+}
+
+template <int DIR, bool NTL, bool NTS, int K, bool SIGNAL>
+__global__ __launch_bounds__(kCopyThreads) void copy_slots_kernel(RunCopyArgs a) {
+  copy_slots_body<DIR, NTL, NTS, K, SIGNAL>(a);
+  if constexpr (SIGNAL) arrive_and_signal(a.arrivals, a.signal, a.signal_delta);
 }
 
 // Head shards when a row piece is a multiple of 1 KiB. TO_BUFFER = split (cache -> shards),
@@ -1382,8 +1454,11 @@ hipError_t launch_copy_runs(int dir, void* const* layer_bases, void* const* dst_
                             int32_t num_layers, int64_t block_bytes, int64_t num_cache_blocks,
                             int64_t dst_num_cache_blocks, const kvx_xfer* xfers,
                             const int64_t* xfer_count, int64_t total_blocks, void* buffer,
-                            int32_t* err, hipStream_t stream) {
+                            int32_t* err, hipStream_t stream, const SignalSpec* signal) {
   RunCopyArgs a;
+  a.signal = signal ? signal->counter : nullptr;
+  a.signal_delta = signal ? signal->delta : 0;
+  a.arrivals = signal ? signal->arrivals : nullptr;
   a.layer_bases = (const char* const*)layer_bases;
   a.dst_layer_bases = (const char* const*)dst_layer_bases;
   a.buffer = (char*)buffer;
@@ -1410,19 +1485,22 @@ hipError_t launch_copy_runs(int dir, void* const* layer_bases, void* const* dst_
   a.num_wgs = ceil_div(a.total_waves, kCopyWavesPerWg);
   a.num_layers = num_layers;
   a.xcd_remap = tuning().xcd_remap;
+  if (signal && (dir == kFromBuffer || a.num_wgs > 0xffffffffll)) return hipErrorInvalidConfiguration;
   const unsigned grid = (unsigned)a.num_wgs;
-#define KVX_COPY_T(NTL, NTS, KB)                                                                \
-  if (slots) copy_slots_kernel<kToBuffer, NTL, NTS, KB><<<grid, kCopyThreads, 0, stream>>>(a); \
-  else copy_runs_kernel<kToBuffer, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
-#define KVX_COPY_F(NTL, NTS, KB)                                                                  \
-  if (slots) copy_slots_kernel<kFromBuffer, NTL, NTS, KB><<<grid, kCopyThreads, 0, stream>>>(a); \
-  else copy_runs_kernel<kFromBuffer, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
-#define KVX_COPY_X(NTL, NTS, KB)                                                              \
-  if (slots) copy_slots_kernel<kDirect, NTL, NTS, KB><<<grid, kCopyThreads, 0, stream>>>(a); \
-  else copy_runs_kernel<kDirect, NTL, NTS><<<grid, kCopyThreads, 0, stream>>>(a);
+#define KVX_COPY_DIR(D, SIG, NTL, NTS, KB)                                                        \
+  if (slots) copy_slots_kernel<D, NTL, NTS, KB, SIG><<<grid, kCopyThreads, 0, stream>>>(a); \
+  else copy_runs_kernel<D, NTL, NTS, SIG><<<grid, kCopyThreads, 0, stream>>>(a);
+#define KVX_COPY_T(NTL, NTS, KB)                                 \
+  if (signal) { KVX_COPY_DIR(kToBuffer, true, NTL, NTS, KB) }    \
+  else { KVX_COPY_DIR(kToBuffer, false, NTL, NTS, KB) }
+#define KVX_COPY_F(NTL, NTS, KB) KVX_COPY_DIR(kFromBuffer, false, NTL, NTS, KB)
+#define KVX_COPY_X(NTL, NTS, KB)                                 \
+  if (signal) { KVX_COPY_DIR(kDirect, true, NTL, NTS, KB) }      \
+  else { KVX_COPY_DIR(kDirect, false, NTL, NTS, KB) }
   if (dir == kToBuffer) { KVX_POLICY_SWITCH(ct.nt_mode, K, KVX_COPY_T) }
   else if (dir == kFromBuffer) { KVX_POLICY_SWITCH(ct.nt_mode, K, KVX_COPY_F) }
   else { KVX_POLICY_SWITCH(ct.nt_mode, K, KVX_COPY_X) }
+#undef KVX_COPY_DIR
 #undef KVX_COPY_T
 #undef KVX_COPY_F
 #undef KVX_COPY_X

@@ -45,14 +45,27 @@ hipError_t launch_build_xfer_list(const int32_t* src_ids, const int32_t* dst_ids
                                   int64_t total_blocks, int32_t mode, kvx_xfer* xfers,
                                   int64_t* xfer_count, int32_t* err, hipStream_t stream);
 
+// A completion signal carried by a copy launch: once every byte of the launch is written and
+// visible device-wide, `delta` is added to *counter. `arrivals` is KVX_ARRIVALS_BYTES of
+// counters that are 0 before the launch; the launch counts its finished workgroups there and
+// leaves them 0 again.
+struct SignalSpec {
+  uint64_t* counter;
+  uint64_t delta;
+  uint32_t* arrivals;
+};
+
 // Run copies: pack (layer_bases -> buffer), single-source unpack (buffer -> layer_bases) or
-// direct (layer_bases -> dst_layer_bases, no buffer).
+// direct (layer_bases -> dst_layer_bases, no buffer). Pack and direct may carry a signal.
 enum { kDirToBuffer = 0, kDirFromBuffer = 1, kDirDirect = 2 };
 hipError_t launch_copy_runs(int dir, void* const* layer_bases, void* const* dst_layer_bases,
                             int32_t num_layers, int64_t block_bytes, int64_t num_cache_blocks,
                             int64_t dst_num_cache_blocks, const kvx_xfer* xfers,
                             const int64_t* xfer_count, int64_t total_blocks, void* buffer,
-                            int32_t* err, hipStream_t stream);
+                            int32_t* err, hipStream_t stream, const SignalSpec* signal = nullptr);
+
+// One-wavefront signal add (kvx_signal.hip): used when a signalling copy has nothing to copy.
+hipError_t launch_signal_add(uint64_t* counter, uint64_t delta, hipStream_t stream);
 
 // head shards: split (to_buffer: cache -> num_shards buffers) or merge (buffers -> cache)
 hipError_t launch_shards(bool to_buffer, void* const* shards, int32_t num_shards,

@@ -22,6 +22,7 @@
 #include <stdint.h>
 
 #include "kvx.h"
+#include "kvx_launch.h"
 
 namespace kvx {
 
@@ -45,6 +46,11 @@ __global__ __launch_bounds__(64) void signal_wait_kernel(const uint64_t* counter
   }
 }
 
+hipError_t launch_signal_add(uint64_t* counter, uint64_t delta, hipStream_t stream) {
+  signal_add_kernel<<<1, 64, 0, stream>>>(counter, delta);
+  return hipGetLastError();
+}
+
 }  // namespace kvx
 
 namespace {
@@ -60,8 +66,7 @@ extern "C" {
 kvx_status kvx_signal_add(uint64_t* counter, uint64_t delta, hipStream_t stream) {
   if (!counter) return KVX_ERR_INVALID_ARGUMENT;
   if (!aligned8(counter)) return KVX_ERR_MISALIGNED;
-  kvx::signal_add_kernel<<<1, 64, 0, stream>>>(counter, delta);
-  return hipGetLastError() == hipSuccess ? KVX_SUCCESS : KVX_ERR_HIP;
+  return kvx::launch_signal_add(counter, delta, stream) == hipSuccess ? KVX_SUCCESS : KVX_ERR_HIP;
 }
 
 kvx_status kvx_signal_wait(const uint64_t* counter, uint64_t value, int64_t timeout_us,

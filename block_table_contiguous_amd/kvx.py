@@ -35,6 +35,7 @@ DEVERR_TIMEOUT = 16
 
 MODE_PACK, MODE_UNPACK, MODE_DIRECT = 0, 1, 2
 MAX_SOURCES = 8
+ARRIVALS_BYTES = 4096  # workspace of one signalling copy (KVX_ARRIVALS_BYTES)
 XFER_BYTES = 32  # sizeof(kvx_xfer)
 
 _P = ctypes.c_void_p
@@ -57,6 +58,9 @@ SIGNATURES = {
     "kvx_copy_direct": (ctypes.c_int, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _I64, _P, _P]),
     "kvx_signal_add": (ctypes.c_int, [_P, ctypes.c_uint64, _P]),
     "kvx_signal_wait": (ctypes.c_int, [_P, ctypes.c_uint64, _I64, _P, _P]),
+    "kvx_pack_signal": (ctypes.c_int, [_P, _I32, _I64, _I64, _P, _P, _I64, _P, _P, ctypes.c_uint64, _P, _P, _P]),
+    "kvx_copy_direct_signal": (ctypes.c_int, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _I64, _P, ctypes.c_uint64,
+                                              _P, _P, _P]),
 }
 
 
@@ -432,6 +436,64 @@ def kvx_unpack_kv_first(send_buf, layer_bases, segment_bytes: int, plane_stride_
                                    req_offsets.numel() - 1, _ptr(xfers), _ptr(xfer_count), int(total_blocks),
                                    _ptr(err_flag), _stream(stream))
     _check("kvx_unpack_kv_first", st)
+
+
+def new_arrivals(device):
+    """A zeroed arrivals workspace for the signalling copies (one per concurrent stream)."""
+    import torch
+
+    return torch.zeros(ARRIVALS_BYTES // 4, dtype=torch.int32, device=device)
+
+
+def _want_signal(counter, arrivals):
+    import torch
+
+    _want(counter, torch.int64, "counter")
+    _want(arrivals, torch.int32, "arrivals")
+    if counter.numel() < 1 or arrivals.numel() * 4 < ARRIVALS_BYTES:
+        raise ValueError(f"kvx: counter needs one element and arrivals {ARRIVALS_BYTES} bytes")
+
+
+def kvx_pack_signal(layer_bases, block_bytes: int, num_cache_blocks: int, xfers, xfer_count,
+                    total_blocks: int, send_buf, counter, arrivals, delta: int = 1, err_flag=None,
+                    stream=None):
+    """kvx_pack whose launch also adds `delta` to `counter` (int64 device tensor, read as
+    uint64) once every packed byte is visible device-wide. `arrivals` is an int32 device
+    tensor of ARRIVALS_BYTES // 4 zeros (new_arrivals); each call leaves it all zero again
+    (one per concurrent stream)."""
+    import torch
+
+    _want(layer_bases, torch.int64, "layer_bases")
+    _want_runs(xfers, xfer_count, total_blocks)
+    _want_signal(counter, arrivals)
+    L = layer_bases.numel()
+    if send_buf.numel() * send_buf.element_size() < L * total_blocks * block_bytes:
+        raise ValueError("kvx: send_buf smaller than num_layers * total_blocks * block_bytes")
+    st = _F["kvx_pack_signal"](_ptr(layer_bases), L, int(block_bytes), int(num_cache_blocks), _ptr(xfers),
+                               _ptr(xfer_count), int(total_blocks), _ptr(send_buf), _ptr(counter), int(delta),
+                               _ptr(arrivals), _ptr(err_flag), _stream(stream))
+    _check("kvx_pack_signal", st)
+
+
+def kvx_copy_direct_signal(src_layer_bases, dst_layer_bases, block_bytes: int, src_num_blocks: int,
+                           dst_num_blocks: int, xfers, xfer_count, total_blocks: int, counter, arrivals,
+                           delta: int = 1, err_flag=None, stream=None):
+    """kvx_copy_direct whose launch also adds `delta` to `counter` once every copied byte is
+    visible device-wide (the one-sided write with its signal); `arrivals` as kvx_pack_signal."""
+    import torch
+
+    _want(src_layer_bases, torch.int64, "src_layer_bases")
+    _want(dst_layer_bases, torch.int64, "dst_layer_bases")
+    _want_runs(xfers, xfer_count, total_blocks)
+    _want_signal(counter, arrivals)
+    L = src_layer_bases.numel()
+    if dst_layer_bases.numel() != L:
+        raise ValueError("kvx: source and destination layer tables differ in length")
+    st = _F["kvx_copy_direct_signal"](_ptr(src_layer_bases), _ptr(dst_layer_bases), L, int(block_bytes),
+                                      int(src_num_blocks), int(dst_num_blocks), _ptr(xfers), _ptr(xfer_count),
+                                      int(total_blocks), _ptr(counter), int(delta), _ptr(arrivals),
+                                      _ptr(err_flag), _stream(stream))
+    _check("kvx_copy_direct_signal", st)
 
 
 def kvx_signal_add(counter, delta: int = 1, stream=None):

@@ -21,7 +21,8 @@
  *     except the int32/int64 index arrays, which need only their natural alignment.
  *   - The call validates its arguments on the host, then enqueues its kernel(s) on `stream`
  *     and returns. It never synchronises, never allocates or frees memory, and keeps no
- *     state between calls (safe to call from several threads). The caller owns all memory
+ *     state between calls (safe to call from several threads); the one exception is the
+ *     arrivals workspace of the signalling copies, which the caller owns. The caller owns all memory
  *     and must keep it alive until the stream work completes.
  *   - Return value: KVX_SUCCESS, or an error detected before anything was enqueued
  *     (KVX_ERR_INVALID_ARGUMENT, KVX_ERR_MISALIGNED, KVX_ERR_CAPACITY), or KVX_ERR_HIP when
@@ -67,6 +68,10 @@ typedef enum kvx_status {
 
 /* Most sources one kvx_unpack call can merge. */
 #define KVX_MAX_SOURCES 8
+
+/* Bytes of the arrivals workspace of one signalling copy (kvx_pack_signal,
+ * kvx_copy_direct_signal). */
+#define KVX_ARRIVALS_BYTES 4096
 
 /* One run (a "contiguous group" of the flagcx page §1.2): num_blocks blocks of one request
  * that are consecutive on the addressed side(s).
@@ -322,6 +327,41 @@ kvx_status kvx_signal_add(uint64_t* counter, uint64_t delta, hipStream_t stream)
 
 kvx_status kvx_signal_wait(const uint64_t* counter, uint64_t value, int64_t timeout_us,
                            int32_t* err_flag, hipStream_t stream);
+
+/*
+ * kvx_pack_signal / kvx_copy_direct_signal — kvx_pack and kvx_copy_direct whose launch also
+ * carries the completion signal ("5. flagcx connector design & dev & test", §1.2: the last
+ * transfer of a batch adds to the receiver's signal counter, putSignal; the receiver's
+ * wait_for_layer_load waits for the count). Same copy, same arguments and errors as the
+ * plain call, plus:
+ *   counter    the uint64 signal counter (device memory, 8-byte aligned), as kvx_signal_add.
+ *              Once every byte this call writes is visible to the whole device, the call
+ *              adds `delta` to it, exactly once. A kvx_signal_wait for the new count (or work
+ *              that reads the counter) therefore sees all of this call's bytes.
+ *   arrivals   KVX_ARRIVALS_BYTES of device memory (128-byte aligned), owned by the caller,
+ *              all zero before the first call; each call counts its finished workgroups
+ *              there (16 group counters and a total, each on its own 128-byte line) and
+ *              leaves it all zero again when it ends. Calls that share an arrivals workspace
+ *              must not run at the same time (enqueue them on one stream); give concurrent
+ *              streams one each. A call that has nothing to copy (num_layers == 0 or
+ *              total_blocks == 0) still adds `delta`.
+ * Used for the per-layer sender pipeline: kvx_pack_signal of layer l with delta 1 replaces
+ * kvx_pack + kvx_signal_add, and saves the separate signal launch.
+ * Errors: as kvx_pack / kvx_copy_direct, plus INVALID_ARGUMENT for a NULL counter or
+ * arrivals, MISALIGNED for a counter not 8-byte or arrivals not 128-byte aligned.
+ */
+kvx_status kvx_pack_signal(void* const* layer_bases, int32_t num_layers, int64_t block_bytes,
+                           int64_t num_cache_blocks, const kvx_xfer* xfers,
+                           const int64_t* xfer_count, int64_t total_blocks, void* send_buf,
+                           uint64_t* counter, uint64_t delta, uint32_t* arrivals,
+                           int32_t* err_flag, hipStream_t stream);
+
+kvx_status kvx_copy_direct_signal(void* const* src_layer_bases, void* const* dst_layer_bases,
+                                  int32_t num_layers, int64_t block_bytes, int64_t src_num_blocks,
+                                  int64_t dst_num_blocks, const kvx_xfer* xfers,
+                                  const int64_t* xfer_count, int64_t total_blocks,
+                                  uint64_t* counter, uint64_t delta, uint32_t* arrivals,
+                                  int32_t* err_flag, hipStream_t stream);
 
 #ifdef __cplusplus
 }

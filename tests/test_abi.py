@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
         "kvx_abi_version", "kvx_build_xfer_list", "kvx_pack", "kvx_reshape_and_cache",
         "kvx_slot_mapping", "kvx_status_string", "kvx_unpack", "kvx_pack_split",
         "kvx_pack_kv_first", "kvx_unpack_kv_first", "kvx_signal_add", "kvx_signal_wait",
-        "kvx_copy_direct"])
+        "kvx_copy_direct", "kvx_pack_signal", "kvx_copy_direct_signal"])
 
 
 def test_every_declared_symbol_is_exported(kvx):
@@ -41,7 +41,7 @@ def test_status_strings(kvx):
         s = kvx.kvx_status_string(code)
         assert s.startswith("kvx: ")
     assert "unknown" in kvx.kvx_status_string(99)
-    assert kvx.kvx_abi_version() == 3
+    assert kvx.kvx_abi_version() == 4
 
 
 def test_xfer_struct_size(kvx):
@@ -227,6 +227,34 @@ def test_copy_direct_validation(kvx):
     assert direct(nbs=0) == kvx.KVX_ERR_INVALID_ARGUMENT  # nothing to read from
     assert direct(bb=8200) == kvx.KVX_ERR_MISALIGNED
     assert direct(n=0, sb=None) == kvx.KVX_SUCCESS
+
+
+def test_signalling_copy_validation(kvx):
+    """The pack and direct copy that carry a completion signal check the counter and the
+    arrivals word first, then everything the plain calls check."""
+    cnt, arr = 0x1000, 0x2000  # fake, suitably aligned device addresses: never dereferenced here
+
+    def pack(lb=P, L=2, bb=8192, nb=100, x=P, c=P, n=10, buf=P, counter=cnt, arrivals=arr):
+        return call(kvx, "kvx_pack_signal", lb, L, bb, nb, x, c, n, buf, counter, 1, arrivals, None, None)
+
+    def direct(sb=P, db=P, L=2, bb=8192, nbs=100, nbd=100, x=P, c=P, n=10, counter=cnt, arrivals=arr):
+        return call(kvx, "kvx_copy_direct_signal", sb, db, L, bb, nbs, nbd, x, c, n, counter, 1, arrivals,
+                    None, None)
+
+    for fn in (pack, direct):
+        assert fn(counter=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+        assert fn(arrivals=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+        assert fn(counter=cnt + 4) == kvx.KVX_ERR_MISALIGNED
+        assert fn(arrivals=arr + 64) == kvx.KVX_ERR_MISALIGNED
+        assert fn(L=-1) == kvx.KVX_ERR_INVALID_ARGUMENT
+        assert fn(bb=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+        assert fn(n=1 << 31) == kvx.KVX_ERR_INVALID_ARGUMENT
+        assert fn(x=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+        assert fn(bb=8200) == kvx.KVX_ERR_MISALIGNED
+    assert pack(buf=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert pack(buf=P + 8) == kvx.KVX_ERR_MISALIGNED
+    assert direct(sb=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert direct(nbs=0) == kvx.KVX_ERR_INVALID_ARGUMENT
 
 
 def _run_python(code, env_extra=None):

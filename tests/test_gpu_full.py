@@ -161,11 +161,12 @@ def test_step_new_token_write_full(pages_caches, stage):
         _progress("step with new-token writes", l, L)
 
 
-def test_layer_pipelined_transfer_full(pages_caches, stage):
+@pytest.mark.parametrize("fused", [False, True], ids=["signal-kernel", "signal-in-pack"])
+def test_layer_pipelined_transfer_full(pages_caches, stage, fused):
     """The contiguous transfer layer by layer at full size: per layer, a bf16 product on a
-    forward stream, then on a copy stream that layer's pack and a signal add, and on a
-    consumer stream the signal wait and that layer's unpack. Checked like the one-launch
-    transfer, every layer whole."""
+    forward stream, then on a copy stream that layer's pack and a signal add (a separate
+    launch, or carried by the pack's own launch), and on a consumer stream the signal wait
+    and that layer's unpack. Checked like the one-launch transfer, every layer whole."""
     spec, src, dst = pages_caches
     case = W.pages_contiguous()
     for t in dst:
@@ -178,6 +179,7 @@ def test_layer_pipelined_transfer_full(pages_caches, stage):
     a = torch.full((2048, 2048), 0.5, dtype=torch.bfloat16, device=DEV)
     c = torch.empty_like(a)
     counter = torch.zeros(1, dtype=torch.int64, device=DEV)
+    arrivals = K.new_arrivals(DEV)
     werr = torch.zeros(1, dtype=torch.int32, device=DEV)
     torch.cuda.synchronize()
     fwd, cpy, cons = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
@@ -187,12 +189,16 @@ def test_layer_pipelined_transfer_full(pages_caches, stage):
             torch.mm(a, a, out=c)
             evs[l].record(fwd)
         cpy.wait_event(evs[l])
-        K.kvx_pack(tr.src_bases[l:l + 1], BB, nb, tr.xp, tr.cp, N, bufv[l], tr.err, stream=cpy)
-        K.kvx_signal_add(counter, 1, stream=cpy)
+        if fused:
+            K.kvx_pack_signal(tr.src_bases[l:l + 1], BB, nb, tr.xp, tr.cp, N, bufv[l], counter, arrivals, 1,
+                              tr.err, stream=cpy)
+        else:
+            K.kvx_pack(tr.src_bases[l:l + 1], BB, nb, tr.xp, tr.cp, N, bufv[l], tr.err, stream=cpy)
+            K.kvx_signal_add(counter, 1, stream=cpy)
         K.kvx_signal_wait(counter, l + 1, 20_000_000, werr, stream=cons)
         K.kvx_unpack([bufv[l]], tr.dst_bases[l:l + 1], BB, nb, 1, tr.xu, tr.cu, N, tr.err, stream=cons)
     torch.cuda.synchronize()
-    assert int(werr.item()) == 0 and int(counter.item()) == L
+    assert int(werr.item()) == 0 and int(counter.item()) == L and not bool(arrivals.any())
     log("layer-pipelined transfer done, checking")
     _verify(case, tr, stage)
 
