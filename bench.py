@@ -16,14 +16,17 @@ One step = one pass of the whole hot path over that batch:
 
 Under "ops", each after evicting the Infinity Cache: the same caches under the other
 block-table shape (fragmented tables for the contiguous headline), as kv-first views, the
-direct cache-to-cache copy, the layer-pipelined pack beside a GEMM forward stand-in, the
-asymmetric-TP head merge and split (32 layers, 64 KiB blocks), and the 32-request decode
+direct cache-to-cache copy, the layer-pipelined pack beside a GEMM forward stand-in (with the
+signal as its own launch or inside the pack's), the asymmetric-TP head merge, a plain unpack
+of the same shape and the head split (32 layers, 64 KiB blocks, each on 3 fresh allocations of
+the destination caches), and the 32-request decode
 slot mapping and new-token write (rows of 8 heads, 2 KiB, and of 1 head, 256 B). "cpu_baseline" is the CPU oracle on the whole step.
 "graph_ms_per_step" is the same step captured once in a HIP graph and replayed (`value`
 stays the eager rate: a graph is fixed to one transfer size).
 
     python bench.py [--steps K] [--warmup W] [--workload contiguous|fragmented]
                     [--no-cpu-baseline] [--no-ops] [--no-pipeline] [--no-graph] [--copy-calib]
+                    [--alloc-spread ROUNDS]
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -72,6 +75,10 @@ def parse():
                     help="skip timing the step replayed from a captured HIP graph (graph_ms_per_step)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--alloc-spread", type=int, default=0, metavar="ROUNDS",
+                    help="only measure how rates move with the physical allocation: ROUNDS times, allocate "
+                         "the 48-layer receive caches and the asymmetric-TP destination caches afresh and "
+                         "time the 48-layer unpack, the head merge and a plain unpack of the merge's shape")
     return ap.parse_args()
 
 
@@ -114,6 +121,47 @@ def copy_calibration(torch, dev):
     print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}), flush=True)
 
 
+def alloc_spread(torch, np, W, K, dev, rounds, reps=3):
+    """Rates against the physical pages an allocation lands on. Sources stay put; each round
+    allocates the 48-layer receive caches (54 GiB) and the asymmetric-TP destination caches
+    (16 GiB) afresh and times, after a cache flush each, the 48-layer unpack, the head merge
+    and a plain unpack of the merge's shape. One JSON line per round on stdout; run it under
+    rocprofv3 --pmc to set counters beside each allocation's rates."""
+    flush = Flush(torch, dev)
+    pc = W.pages_contiguous()
+    sp = pc.src_spec
+    L, nb, BB, N = sp.num_layers, sp.num_blocks, sp.block_bytes, pc.total_blocks
+    did, ro = K.flatten_tables(pc.dst_tables, dev)
+    xu, cu = K.new_xfer_list(N, dev)
+    K.kvx_build_xfer_list(None, did, ro, K.MODE_UNPACK, xu, cu)
+    buf = W.fill_device_random_(torch.empty(L * N * BB, dtype=torch.uint8, device=dev), pc.seed)
+    ac = W.asym_tp()
+    La, Na, S = ac.dst_spec.num_layers, ac.total_blocks, ac.num_src
+    BBa, nba = ac.dst_spec.block_bytes, ac.dst_spec.num_blocks
+    srcs = [W.fill_device_random_(torch.empty((La, Na, BBa // S), dtype=torch.uint8, device=dev), ac.seed * 10 + s)
+            for s in range(S)]
+    one = W.fill_device_random_(torch.empty((La, Na, BBa), dtype=torch.uint8, device=dev), ac.seed * 10 + 7)
+    aid, aro = K.flatten_tables(ac.dst_tables, dev)
+    xa, ca = K.new_xfer_list(Na, dev)
+    K.kvx_build_xfer_list(None, aid, aro, K.MODE_UNPACK, xa, ca)
+    ub, mb = 2 * L * N * BB, 2 * La * Na * BBa
+    for rnd in range(rounds):
+        dst = [W.fill_device_byte_(torch.empty((nb, BB), dtype=torch.uint8, device=dev)) for _ in range(L)]
+        adst = [W.fill_device_byte_(torch.empty((nba, BBa), dtype=torch.uint8, device=dev)) for _ in range(La)]
+        db, adb = K.layer_base_table(dst), K.layer_base_table(adst)
+        torch.cuda.synchronize()
+        rates = {}
+        for name, nbytes, fn in (
+                ("unpack_48layer", ub, lambda: K.kvx_unpack([buf], db, BB, nb, 1, xu, cu, N)),
+                ("merge_asym_tp", mb, lambda: K.kvx_unpack(srcs, adb, BBa, nba, ac.rows_per_block, xa, ca, Na)),
+                ("unpack_asym_tp_shape", mb, lambda: K.kvx_unpack([one], adb, BBa, nba, 1, xa, ca, Na))):
+            med, _ = time_op(torch, fn, reps, flush)
+            rates[name] = round(nbytes / (med * 1e-3) / 1e9, 1)
+        print(json.dumps({"round": rnd, "GB/s": rates}), flush=True)
+        del dst, adst, db, adb
+        torch.cuda.empty_cache()
+
+
 def traffic_from_counters(name: str, launches_bytes: int):
     """HBM bytes per launch of `name` from the committed rocprofv3 counter summary, scaled by
     the copy-kernel calibration; None if absent or taken on other kernel sources."""
@@ -149,6 +197,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_calib:
         copy_calibration(torch, dev)
+        return
+    if args.alloc_spread:
+        alloc_spread(torch, np, W, K, dev, args.alloc_spread)
         return
 
     case = W.pages_contiguous() if args.workload == "contiguous" else W.pages_fragmented()
@@ -402,6 +453,8 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
       inline        per layer on the forward stream: the product, the pack of that layer into
                     its slice of the send buffer, and a signal add (the count a transport, or a
                     receiver's signal wait, follows layer by layer);
+      inline_fused  the same, with the signal carried by the pack's own launch
+                    (kvx_pack_signal) instead of a separate signal kernel;
       pipelined     per layer: the product, then an event on the forward stream; on a copy
                     stream, a wait for that event, the layer's pack and the signal add. The
                     forward stream never waits for a copy.
@@ -445,6 +498,17 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
                 K.kvx_signal_add(counter, 1, stream=fwd)
                 rdy[l].record(fwd)
 
+    arrivals = K.new_arrivals(dev)
+
+    def inline_fused(f_ev, rdy):
+        with torch.cuda.stream(fwd):
+            for l in range(L):
+                layer_forward(l)
+                if l == L - 1:
+                    f_ev.record(fwd)
+                K.kvx_pack_signal(pack_l[l], BB, nb, xp, cp, N, bufv[l], counter, arrivals, 1, err, stream=fwd)
+                rdy[l].record(fwd)
+
     def pipelined(f_ev, rdy):
         for l in range(L):
             with torch.cuda.stream(fwd):
@@ -469,15 +533,15 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
         total = s_ev.elapsed_time(e_ev)
         # one launch packs every layer in the schedules without per-layer events: all of its
         # layers are complete when it ends
-        ready = (sum(s_ev.elapsed_time(r) for r in rdy) / L) if fn in (inline, pipelined) else total
+        ready = (sum(s_ev.elapsed_time(r) for r in rdy) / L) if fn in (inline, inline_fused, pipelined) else total
         return total, f_ev.elapsed_time(e_ev), ready
 
     out = {"workload": f"{L} layers; forward stream: one bf16 [{m}x{k}]x[{k}x{k}] product per layer with "
                        "its own weight, output feeding the next layer (forward stand-in); per layer: that "
-                       "layer's pack, then a signal add (inline on the forward stream, or pipelined on a "
-                       "copy stream)"}
+                       "layer's pack, then a signal add (inline on the forward stream, inline with the signal "
+                       "in the pack's launch, or pipelined on a copy stream)"}
     for name, fn in (("forward_only", forward_only), ("serial", serial), ("inline", inline),
-                     ("pipelined", pipelined)):
+                     ("inline_fused", inline_fused), ("pipelined", pipelined)):
         run(fn)  # warm
         ts = sorted(run(fn) for _ in range(reps))
         total, tail, ready = ts[len(ts) // 2]
@@ -489,54 +553,67 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
             f"mean layer ready {ready:.4f} ms")
     torch.cuda.synchronize()
     assert int(err.item()) == 0, "device error flag raised"
-    assert int(counter.item()) == 2 * L * (reps + 1), "signal count"
+    assert int(counter.item()) == 3 * L * (reps + 1), "signal count"
+    assert not bool(arrivals.any()), "arrivals workspace left non-zero"
     return out
 
 
-def other_workloads(torch, np, W, K, dev, flush, reps):
+def other_workloads(torch, np, W, K, dev, flush, reps, allocs=3):
     """The rows the headline batch does not exercise, each on its own workload."""
     out = {}
-    # asymmetric-TP receive: 2 sources x 4 heads -> 8-head caches, 32 layers x 4096 blocks
+    # asymmetric-TP receive: 2 sources x 4 heads -> 8-head caches, 32 layers x 4096 blocks.
+    # Rates of this shape move by up to +-10% with the physical pages an allocation lands on
+    # (5.5-6.6 TB/s for the same code in one process), so the destination caches are
+    # allocated afresh `allocs` times and each op reports the median over the allocations of
+    # its median over reps, with every allocation's rate beside it.
     case = W.asym_tp()
     L, N, S = case.dst_spec.num_layers, case.total_blocks, case.num_src
     BB, nb = case.dst_spec.block_bytes, case.dst_spec.num_blocks
     srcs = [torch.empty((L, N, BB // S), dtype=torch.uint8, device=dev) for _ in range(S)]
-    for s, t in enumerate(srcs):
-        W.fill_device_random_(t, case.seed * 10 + s)
-    dst = [W.fill_device_byte_(torch.empty((nb, BB), dtype=torch.uint8, device=dev)) for _ in range(L)]
-    bases = K.layer_base_table(dst)
+    for s_, t in enumerate(srcs):
+        W.fill_device_random_(t, case.seed * 10 + s_)
+    one = torch.empty((L, N, BB), dtype=torch.uint8, device=dev)
+    W.fill_device_random_(one, case.seed * 10 + 7)
     ids, ro = K.flatten_tables(case.dst_tables, dev)
     x, c = K.new_xfer_list(N, dev)
     K.kvx_build_xfer_list(None, ids, ro, K.MODE_UNPACK, x, c)
-    med, mn = time_op(torch, lambda: K.kvx_unpack(srcs, bases, BB, nb, case.rows_per_block, x, c, N), reps, flush)
-    nbytes = 2 * L * N * BB
-    out["merge_unpack_asym_tp"] = {
-        "workload": "2 sources x 4 of 8 heads, 32 layers x 16 requests x 256 blocks -> [8192][16][K,V][8][128] bf16",
-        "bytes": nbytes, "median_ms": round(med, 4), "min_ms": round(mn, 4),
-        "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "traffic": traffic_from_counters("merge_asym_tp", nbytes)}
-    # the same destination blocks and bytes from one full-head buffer: a plain unpack, the
-    # merge's own shape without the head interleave (its cost against the merge's)
-    one = torch.empty((L, N, BB), dtype=torch.uint8, device=dev)
-    W.fill_device_random_(one, case.seed * 10 + 7)
-    med, mn = time_op(torch, lambda: K.kvx_unpack([one], bases, BB, nb, 1, x, c, N), reps, flush)
-    out["unpack_asym_tp_shape"] = {
-        "workload": "one buffer of all 8 heads, 32 layers x 16 requests x 256 blocks -> the same [8192][16][K,V][8][128] "
-                    "bf16 caches and destination ids as the merge",
-        "bytes": nbytes, "median_ms": round(med, 4), "min_ms": round(mn, 4),
-        "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "traffic": traffic_from_counters("unpack_asym_tp_shape", nbytes)}
-    del one
-    # the sender side of the same shapes: full-head caches split into 2 head shards
     xs, cs = K.new_xfer_list(N, dev)
     K.kvx_build_xfer_list(ids, None, ro, K.MODE_PACK, xs, cs)
-    med, mn = time_op(torch, lambda: K.kvx_pack_split(bases, BB, nb, case.rows_per_block, xs, cs, N, srcs), reps, flush)
-    out["split_pack_asym_tp"] = {
-        "workload": "32 layers of [8192][16][K,V][8][128] bf16, 16 requests x 256 blocks -> 2 shards x 4 heads",
-        "bytes": nbytes, "median_ms": round(med, 4), "min_ms": round(mn, 4),
-        "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "traffic": traffic_from_counters("split_asym_tp", nbytes)}
-    del srcs, dst
+    nbytes = 2 * L * N * BB
+    per = {"merge": [], "plain": [], "split": []}
+    for _ in range(allocs):
+        dst = [W.fill_device_byte_(torch.empty((nb, BB), dtype=torch.uint8, device=dev)) for _ in range(L)]
+        bases = K.layer_base_table(dst)
+        for name, fn in (("merge", lambda: K.kvx_unpack(srcs, bases, BB, nb, case.rows_per_block, x, c, N)),
+                         ("plain", lambda: K.kvx_unpack([one], bases, BB, nb, 1, x, c, N)),
+                         ("split", lambda: K.kvx_pack_split(bases, BB, nb, case.rows_per_block, xs, cs, N, srcs))):
+            med, _ = time_op(torch, fn, reps, flush)
+            per[name].append(med)
+        del dst, bases
+        torch.cuda.empty_cache()
+    del srcs, one
+    torch.cuda.empty_cache()
+
+    def shape_op(name, workload, counters):
+        ms = sorted(per[name])
+        med = ms[len(ms) // 2]
+        return {"workload": workload, "bytes": nbytes, "allocations": allocs, "median_ms": round(med, 4),
+                "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "per_allocation_GB/s": [round(nbytes / (t * 1e-3) / 1e9, 1) for t in per[name]],
+                "traffic": traffic_from_counters(counters, nbytes)}
+    out["merge_unpack_asym_tp"] = shape_op(
+        "merge", "2 sources x 4 of 8 heads, 32 layers x 16 requests x 256 blocks -> [8192][16][K,V][8][128] bf16",
+        "merge_asym_tp")
+    # the same destination blocks and bytes from one full-head buffer: a plain unpack, the
+    # merge's own shape without the head interleave (its cost against the merge's)
+    out["unpack_asym_tp_shape"] = shape_op(
+        "plain", "one buffer of all 8 heads, 32 layers x 16 requests x 256 blocks -> the same [8192][16][K,V][8][128] "
+                 "bf16 caches and destination ids as the merge", "unpack_asym_tp_shape")
+    # the sender side of the same shapes: full-head caches split into 2 head shards
+    out["split_pack_asym_tp"] = shape_op(
+        "split", "32 layers of [8192][16][K,V][8][128] bf16, 16 requests x 256 blocks -> 2 shards x 4 heads",
+        "split_asym_tp")
     # decode write: 32 requests of 1..2048 tokens into a [4096][16][K,V][8][128] bf16 cache
     d = W.decode_write()
     T = len(d.req_idx)
