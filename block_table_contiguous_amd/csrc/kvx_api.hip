@@ -4,8 +4,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kvx.h"
 #include "kvx_launch.h"
+
+// The allocation-free signalling pack keeps its arrivals workspaces here: KVX_NOALLOC_SLOTS
+// workspaces of KVX_ARRIVALS_BYTES per GPU (64 KiB), zero when the library is loaded and left
+// zero by every call that completes. In host code `scratch` only names the variable; its
+// device address on each GPU comes from hipGetSymbolAddress (scratch_words below) and is the
+// only form of it passed to kernels.
+static __device__ __align__(256) uint32_t scratch[KVX_NOALLOC_SLOTS * (KVX_ARRIVALS_BYTES / 4)];
 
 namespace {
 
@@ -16,6 +25,27 @@ inline kvx_status from_hip(hipError_t e) { return e == hipSuccess ? KVX_SUCCESS 
 
 constexpr int64_t kMaxBlocks = 0x7fffffff;  // block ids and run lengths are int32
 
+// Device address of `scratch` on the GPU that owns `stream`, looked up once per device (with
+// that device current: the call requires it) and kept. No allocation is involved.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t* g_scratch[kMaxDevices] = {};
+
+kvx_status scratch_words(hipStream_t stream, uint32_t** out) {
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &dev) != hipSuccess)
+    return KVX_ERR_HIP;
+  if (dev != cur || dev < 0 || dev >= kMaxDevices) return KVX_ERR_INVALID_ARGUMENT;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVX_ERR_HIP;
+    g_scratch[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = g_scratch[dev];
+  return KVX_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -25,13 +55,13 @@ const char* kvx_status_string(kvx_status status) {
     case KVX_SUCCESS: return "kvx: success";
     case KVX_ERR_INVALID_ARGUMENT: return "kvx: invalid argument (null pointer, negative size or bad mode)";
     case KVX_ERR_MISALIGNED: return "kvx: pointer, size or stride not a multiple of 16 bytes";
-    case KVX_ERR_CAPACITY: return "kvx: output array smaller than the worst case";
+    case KVX_ERR_CAPACITY: return "kvx: output array smaller than the worst case, or request beyond the library's fixed scratch";
     case KVX_ERR_HIP: return "kvx: HIP kernel launch failed";
   }
   return "kvx: unknown status";
 }
 
-int32_t kvx_abi_version(void) { return 4; }
+int32_t kvx_abi_version(void) { return 5; }
 
 kvx_status kvx_slot_mapping(const int32_t* block_table, int64_t num_reqs,
                             int64_t max_blocks_per_req, int64_t bt_row_stride,
@@ -222,6 +252,30 @@ kvx_status kvx_copy_direct_signal(void* const* src_layer_bases, void* const* dst
                                         num_layers, block_bytes, src_num_blocks, dst_num_blocks,
                                         xfers, xfer_count, total_blocks, nullptr, err_flag, stream,
                                         &sig));
+}
+
+kvx_status kvx_pack_signal_noalloc(void* const* layer_bases, int32_t num_layers, int64_t block_bytes,
+                                   int64_t num_cache_blocks, const kvx_xfer* xfers,
+                                   const int64_t* xfer_count, int64_t total_blocks, void* send_buf,
+                                   uint64_t* counter, uint64_t delta, int32_t slot,
+                                   int32_t* err_flag, hipStream_t stream) {
+  if (slot < 0 || slot >= KVX_NOALLOC_SLOTS) return KVX_ERR_CAPACITY;
+  if (!counter) return KVX_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)counter & 7u) != 0) return KVX_ERR_MISALIGNED;
+  if (num_layers < 0 || block_bytes <= 0 || num_cache_blocks < 0 || total_blocks < 0 ||
+      total_blocks > kMaxBlocks)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (num_layers == 0 || total_blocks == 0)
+    return from_hip(kvx::launch_signal_add(counter, delta, stream));
+  if (!layer_bases || !xfers || !xfer_count || !send_buf) return KVX_ERR_INVALID_ARGUMENT;
+  if (!mult16(block_bytes) || !aligned16(send_buf)) return KVX_ERR_MISALIGNED;
+  uint32_t* words = nullptr;
+  const kvx_status st = scratch_words(stream, &words);
+  if (st != KVX_SUCCESS) return st;
+  const kvx::SignalSpec sig = {counter, delta, words + (int64_t)slot * (KVX_ARRIVALS_BYTES / 4)};
+  return from_hip(kvx::launch_copy_runs(kvx::kDirToBuffer, layer_bases, nullptr, num_layers,
+                                        block_bytes, num_cache_blocks, 0, xfers, xfer_count,
+                                        total_blocks, send_buf, err_flag, stream, &sig));
 }
 
 static kvx_status kv_first_checks(void* const* layer_bases, int32_t num_layers,

@@ -36,6 +36,7 @@ DEVERR_TIMEOUT = 16
 MODE_PACK, MODE_UNPACK, MODE_DIRECT = 0, 1, 2
 MAX_SOURCES = 8
 ARRIVALS_BYTES = 4096  # workspace of one signalling copy (KVX_ARRIVALS_BYTES)
+NOALLOC_SLOTS = 16  # arrivals workspaces the library keeps per GPU for kvx_pack_signal_noalloc
 XFER_BYTES = 32  # sizeof(kvx_xfer)
 
 _P = ctypes.c_void_p
@@ -61,6 +62,8 @@ SIGNATURES = {
     "kvx_pack_signal": (ctypes.c_int, [_P, _I32, _I64, _I64, _P, _P, _I64, _P, _P, ctypes.c_uint64, _P, _P, _P]),
     "kvx_copy_direct_signal": (ctypes.c_int, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _I64, _P, ctypes.c_uint64,
                                               _P, _P, _P]),
+    "kvx_pack_signal_noalloc": (ctypes.c_int, [_P, _I32, _I64, _I64, _P, _P, _I64, _P, _P, ctypes.c_uint64, _I32,
+                                               _P, _P]),
 }
 
 
@@ -473,6 +476,27 @@ def kvx_pack_signal(layer_bases, block_bytes: int, num_cache_blocks: int, xfers,
                                _ptr(xfer_count), int(total_blocks), _ptr(send_buf), _ptr(counter), int(delta),
                                _ptr(arrivals), _ptr(err_flag), _stream(stream))
     _check("kvx_pack_signal", st)
+
+
+def kvx_pack_signal_noalloc(layer_bases, block_bytes: int, num_cache_blocks: int, xfers, xfer_count,
+                            total_blocks: int, send_buf, counter, slot: int = 0, delta: int = 1, err_flag=None,
+                            stream=None):
+    """kvx_pack_signal with the arrivals workspace taken from the library's own static array
+    (workspace `slot` of NOALLOC_SLOTS): nothing is allocated, here or in the library. Calls
+    that use the same slot must not overlap in time; the stream must belong to the current
+    device."""
+    import torch
+
+    _want(layer_bases, torch.int64, "layer_bases")
+    _want_runs(xfers, xfer_count, total_blocks)
+    _want(counter, torch.int64, "counter")
+    L = layer_bases.numel()
+    if send_buf.numel() * send_buf.element_size() < L * total_blocks * block_bytes:
+        raise ValueError("kvx: send_buf smaller than num_layers * total_blocks * block_bytes")
+    st = _F["kvx_pack_signal_noalloc"](_ptr(layer_bases), L, int(block_bytes), int(num_cache_blocks), _ptr(xfers),
+                                       _ptr(xfer_count), int(total_blocks), _ptr(send_buf), _ptr(counter),
+                                       int(delta), int(slot), _ptr(err_flag), _stream(stream))
+    _check("kvx_pack_signal_noalloc", st)
 
 
 def kvx_copy_direct_signal(src_layer_bases, dst_layer_bases, block_bytes: int, src_num_blocks: int,

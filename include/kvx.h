@@ -22,7 +22,8 @@
  *   - The call validates its arguments on the host, then enqueues its kernel(s) on `stream`
  *     and returns. It never synchronises, never allocates or frees memory, and keeps no
  *     state between calls (safe to call from several threads); the one exception is the
- *     arrivals workspace of the signalling copies, which the caller owns. The caller owns all memory
+ *     arrivals workspace of the signalling copies, which the caller owns (or, for
+ *     kvx_pack_signal_noalloc, the library's static array). The caller owns all memory
  *     and must keep it alive until the stream work completes.
  *   - Return value: KVX_SUCCESS, or an error detected before anything was enqueued
  *     (KVX_ERR_INVALID_ARGUMENT, KVX_ERR_MISALIGNED, KVX_ERR_CAPACITY), or KVX_ERR_HIP when
@@ -49,7 +50,8 @@ typedef enum kvx_status {
   KVX_SUCCESS = 0,
   KVX_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, negative size, bad mode, ... */
   KVX_ERR_MISALIGNED = 2,       /* a pointer, size or stride is not a multiple of 16    */
-  KVX_ERR_CAPACITY = 3,         /* an output array is smaller than the worst case       */
+  KVX_ERR_CAPACITY = 3,         /* an output array is smaller than the worst case, or a
+                                   request goes past the library's fixed scratch          */
   KVX_ERR_HIP = 4               /* the HIP launch failed                                */
 } kvx_status;
 
@@ -72,6 +74,9 @@ typedef enum kvx_status {
 /* Bytes of the arrivals workspace of one signalling copy (kvx_pack_signal,
  * kvx_copy_direct_signal). */
 #define KVX_ARRIVALS_BYTES 4096
+
+/* Arrivals workspaces the library keeps per GPU for kvx_pack_signal_noalloc. */
+#define KVX_NOALLOC_SLOTS 16
 
 /* One run (a "contiguous group" of the flagcx page §1.2): num_blocks blocks of one request
  * that are consecutive on the addressed side(s).
@@ -362,6 +367,30 @@ kvx_status kvx_copy_direct_signal(void* const* src_layer_bases, void* const* dst
                                   const int64_t* xfer_count, int64_t total_blocks,
                                   uint64_t* counter, uint64_t delta, uint32_t* arrivals,
                                   int32_t* err_flag, hipStream_t stream);
+
+/*
+ * kvx_pack_signal_noalloc — kvx_pack_signal for callers that cannot allocate, not even the
+ * arrivals workspace: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same copy, signal, arguments and errors as kvx_pack_signal, except that the
+ * arrivals workspace is workspace `slot` of the library's own static array of
+ * KVX_NOALLOC_SLOTS workspaces of KVX_ARRIVALS_BYTES per GPU (64 KiB, held by each GPU the
+ * library runs on until the process ends).
+ *   slot       0 <= slot < KVX_NOALLOC_SLOTS, else KVX_ERR_CAPACITY before anything else.
+ *              Every call on one GPU that uses the same slot shares that workspace: such
+ *              calls must not overlap in time (enqueue them on one stream) or they race.
+ *              Calls on different slots may run concurrently, e.g. one slot per sender
+ *              stream. The workspaces are zero when the library is loaded and every completed
+ *              call leaves its workspace zero, as kvx_pack_signal leaves its own.
+ *   stream     must belong to the current device (KVX_ERR_INVALID_ARGUMENT otherwise): the
+ *              first call on each device looks up the array's address on that device once,
+ *              with hipGetSymbolAddress, and keeps it.
+ * Allocates nothing, frees nothing, and never synchronises.
+ */
+kvx_status kvx_pack_signal_noalloc(void* const* layer_bases, int32_t num_layers, int64_t block_bytes,
+                                   int64_t num_cache_blocks, const kvx_xfer* xfers,
+                                   const int64_t* xfer_count, int64_t total_blocks, void* send_buf,
+                                   uint64_t* counter, uint64_t delta, int32_t slot,
+                                   int32_t* err_flag, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
         "kvx_abi_version", "kvx_build_xfer_list", "kvx_pack", "kvx_reshape_and_cache",
         "kvx_slot_mapping", "kvx_status_string", "kvx_unpack", "kvx_pack_split",
         "kvx_pack_kv_first", "kvx_unpack_kv_first", "kvx_signal_add", "kvx_signal_wait",
-        "kvx_copy_direct", "kvx_pack_signal", "kvx_copy_direct_signal"])
+        "kvx_copy_direct", "kvx_pack_signal", "kvx_copy_direct_signal", "kvx_pack_signal_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(kvx):
@@ -41,7 +41,7 @@ def test_status_strings(kvx):
         s = kvx.kvx_status_string(code)
         assert s.startswith("kvx: ")
     assert "unknown" in kvx.kvx_status_string(99)
-    assert kvx.kvx_abi_version() == 4
+    assert kvx.kvx_abi_version() == 5
 
 
 def test_xfer_struct_size(kvx):
@@ -255,6 +255,25 @@ def test_signalling_copy_validation(kvx):
     assert pack(buf=P + 8) == kvx.KVX_ERR_MISALIGNED
     assert direct(sb=None) == kvx.KVX_ERR_INVALID_ARGUMENT
     assert direct(nbs=0) == kvx.KVX_ERR_INVALID_ARGUMENT
+
+
+def test_allocation_free_pack_validation(kvx):
+    """The allocation-free signalling pack refuses a slot outside the library's array before
+    anything else, then checks what kvx_pack_signal checks; none of this touches HIP."""
+    def pack(slot=0, counter=0x1000, L=2, bb=8192, n=10, buf=P, x=P):
+        return call(kvx, "kvx_pack_signal_noalloc", P, L, bb, 100, x, P, n, buf, counter, 1, slot, None, None)
+
+    assert kvx.NOALLOC_SLOTS == 16
+    assert pack(slot=-1) == kvx.KVX_ERR_CAPACITY
+    assert pack(slot=16) == kvx.KVX_ERR_CAPACITY
+    assert pack(slot=16, counter=None) == kvx.KVX_ERR_CAPACITY
+    assert pack(counter=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert pack(counter=0x1004) == kvx.KVX_ERR_MISALIGNED
+    assert pack(L=-1) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert pack(x=None) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert pack(bb=8200) == kvx.KVX_ERR_MISALIGNED
+    assert pack(buf=P + 8) == kvx.KVX_ERR_MISALIGNED
+    assert "scratch" in kvx.kvx_status_string(kvx.KVX_ERR_CAPACITY)
 
 
 def _run_python(code, env_extra=None):
