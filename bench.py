@@ -465,7 +465,9 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
                     (kvx_pack_signal) instead of a separate signal kernel;
       pipelined     per layer: the product, then an event on the forward stream; on a copy
                     stream, a wait for that event, the layer's pack and the signal add. The
-                    forward stream never waits for a copy.
+                    forward stream never waits for a copy;
+      pipelined_fused  the same on the copy stream with the signal carried by the pack's own
+                    launch (kvx_pack_signal): one launch per layer beside the forward.
     Per schedule: the total, the tail (end of the last product to the end of the packing) and
     mean_ready (start to the moment a layer's packed bytes are complete, averaged over the
     layers: when a transport could begin sending each layer). The receiver's unpack is left
@@ -528,6 +530,16 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
             rdy[l].record(cpy)
         f_ev.record(fwd)
 
+    def pipelined_fused(f_ev, rdy):
+        for l in range(L):
+            with torch.cuda.stream(fwd):
+                layer_forward(l)
+                evs[l].record(fwd)
+            cpy.wait_event(evs[l])
+            K.kvx_pack_signal(pack_l[l], BB, nb, xp, cp, N, bufv[l], counter, arrivals, 1, err, stream=cpy)
+            rdy[l].record(cpy)
+        f_ev.record(fwd)
+
     def run(fn):
         torch.cuda.synchronize()
         s_ev, f_ev, e_ev = (torch.cuda.Event(enable_timing=True) for _ in range(3))
@@ -541,15 +553,16 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
         total = s_ev.elapsed_time(e_ev)
         # one launch packs every layer in the schedules without per-layer events: all of its
         # layers are complete when it ends
-        ready = (sum(s_ev.elapsed_time(r) for r in rdy) / L) if fn in (inline, inline_fused, pipelined) else total
+        ready = (sum(s_ev.elapsed_time(r) for r in rdy) / L) if fn in (inline, inline_fused, pipelined, pipelined_fused) else total
         return total, f_ev.elapsed_time(e_ev), ready
 
     out = {"workload": f"{L} layers; forward stream: one bf16 [{m}x{k}]x[{k}x{k}] product per layer with "
                        "its own weight, output feeding the next layer (forward stand-in); per layer: that "
-                       "layer's pack, then a signal add (inline on the forward stream, inline with the signal "
-                       "in the pack's launch, or pipelined on a copy stream)"}
+                       "layer's pack, then a signal add (inline on the forward stream or pipelined on a copy "
+                       "stream; each either as a separate signal kernel or carried by the pack's own launch)"}
     for name, fn in (("forward_only", forward_only), ("serial", serial), ("inline", inline),
-                     ("inline_fused", inline_fused), ("pipelined", pipelined)):
+                     ("inline_fused", inline_fused), ("pipelined", pipelined),
+                     ("pipelined_fused", pipelined_fused)):
         run(fn)  # warm
         ts = sorted(run(fn) for _ in range(reps))
         total, tail, ready = ts[len(ts) // 2]
@@ -561,7 +574,7 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
             f"mean layer ready {ready:.4f} ms")
     torch.cuda.synchronize()
     assert int(err.item()) == 0, "device error flag raised"
-    assert int(counter.item()) == 3 * L * (reps + 1), "signal count"
+    assert int(counter.item()) == 4 * L * (reps + 1), "signal count"
     assert not bool(arrivals.any()), "arrivals workspace left non-zero"
     return out
 
