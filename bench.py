@@ -76,9 +76,10 @@ def parse():
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     ap.add_argument("--alloc-spread", type=int, default=0, metavar="ROUNDS",
-                    help="only measure how rates move with the physical allocation: ROUNDS times, allocate "
-                         "the 48-layer receive caches and the asymmetric-TP destination caches afresh and "
-                         "time the 48-layer unpack, the head merge and a plain unpack of the merge's shape")
+                    help="only measure how rates move with where the destination caches sit in memory: "
+                         "ROUNDS placements of the 48-layer receive caches and the asymmetric-TP destination "
+                         "caches inside one 198 GiB pool, each timing the 48-layer unpack, the head merge and "
+                         "a plain unpack of the merge's shape")
     return ap.parse_args()
 
 
@@ -122,11 +123,14 @@ def copy_calibration(torch, dev):
 
 
 def alloc_spread(torch, np, W, K, dev, rounds, reps=3):
-    """Rates against the physical pages an allocation lands on. Sources stay put; each round
-    allocates the 48-layer receive caches (54 GiB) and the asymmetric-TP destination caches
-    (16 GiB) afresh and times, after a cache flush each, the 48-layer unpack, the head merge
-    and a plain unpack of the merge's shape. One JSON line per round on stdout; run it under
-    rocprofv3 --pmc to set counters beside each allocation's rates."""
+    """Rates against where the destination caches sit in memory, all in one process. Sources
+    stay put. One pool of 176 chunks of 1.125 GiB (198 GiB) is allocated and filled once;
+    placement r puts the 48 receive layers of the 48-layer unpack in chunks [r*s, r*s + 48) and
+    the 32 destination layers of the asymmetric-TP workload in the first 16 of those chunks (two
+    512 MiB layers per chunk), with the stride s spreading the placements over the pool. Per
+    placement, after a cache flush each: the 48-layer unpack, the head merge and a plain unpack
+    of the merge's shape (median of reps). One JSON line per placement; run it under
+    rocprofv3 --pmc to set counters beside each placement's rates."""
     flush = Flush(torch, dev)
     pc = W.pages_contiguous()
     sp = pc.src_spec
@@ -138,18 +142,23 @@ def alloc_spread(torch, np, W, K, dev, rounds, reps=3):
     ac = W.asym_tp()
     La, Na, S = ac.dst_spec.num_layers, ac.total_blocks, ac.num_src
     BBa, nba = ac.dst_spec.block_bytes, ac.dst_spec.num_blocks
+    assert 2 * nba * BBa <= nb * BB and La <= 2 * L
     srcs = [W.fill_device_random_(torch.empty((La, Na, BBa // S), dtype=torch.uint8, device=dev), ac.seed * 10 + s)
             for s in range(S)]
     one = W.fill_device_random_(torch.empty((La, Na, BBa), dtype=torch.uint8, device=dev), ac.seed * 10 + 7)
     aid, aro = K.flatten_tables(ac.dst_tables, dev)
     xa, ca = K.new_xfer_list(Na, dev)
     K.kvx_build_xfer_list(None, aid, aro, K.MODE_UNPACK, xa, ca)
+    chunks = 176
+    pool = [W.fill_device_byte_(torch.empty((nb, BB), dtype=torch.uint8, device=dev)) for _ in range(chunks)]
+    step = (chunks - L) // max(rounds - 1, 1)
     ub, mb = 2 * L * N * BB, 2 * La * Na * BBa
+    torch.cuda.synchronize()
     for rnd in range(rounds):
-        dst = [W.fill_device_byte_(torch.empty((nb, BB), dtype=torch.uint8, device=dev)) for _ in range(L)]
-        adst = [W.fill_device_byte_(torch.empty((nba, BBa), dtype=torch.uint8, device=dev)) for _ in range(La)]
+        first = min(rnd * step, chunks - L)
+        dst = pool[first:first + L]
+        adst = [dst[i // 2].view(-1)[(i % 2) * nba * BBa:(i % 2 + 1) * nba * BBa].view(nba, BBa) for i in range(La)]
         db, adb = K.layer_base_table(dst), K.layer_base_table(adst)
-        torch.cuda.synchronize()
         rates = {}
         for name, nbytes, fn in (
                 ("unpack_48layer", ub, lambda: K.kvx_unpack([buf], db, BB, nb, 1, xu, cu, N)),
@@ -157,9 +166,7 @@ def alloc_spread(torch, np, W, K, dev, rounds, reps=3):
                 ("unpack_asym_tp_shape", mb, lambda: K.kvx_unpack([one], adb, BBa, nba, 1, xa, ca, Na))):
             med, _ = time_op(torch, fn, reps, flush)
             rates[name] = round(nbytes / (med * 1e-3) / 1e9, 1)
-        print(json.dumps({"round": rnd, "GB/s": rates}), flush=True)
-        del dst, adst, db, adb
-        torch.cuda.empty_cache()
+        print(json.dumps({"round": rnd, "chunks": [first, first + L - 1], "GB/s": rates}), flush=True)
 
 
 def traffic_from_counters(name: str, launches_bytes: int):

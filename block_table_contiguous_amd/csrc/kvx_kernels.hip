@@ -30,22 +30,19 @@ static int64_t env_i64(const char* name, int64_t dflt) {
   return (end && *end == '\0') ? (int64_t)v : dflt;
 }
 
-// Cache policy: copies of 8 KiB blocks load non-temporally and store with the default policy
-// (1); the head merge and split, whose blocks are 64 KiB, do both non-temporally (3). Each was
-// the faster of the two on every op in interleaved A/B runs over three sets of allocations.
 const Tuning& tuning() {
   static const Tuning t = {
-      {env_i64("KVX_WAVE_BYTES_PACK", 8 * 1024), (int)env_i64("KVX_NT_PACK", 1),
+      {env_i64("KVX_WAVE_BYTES_PACK", 8 * 1024), (int)env_i64("KVX_NT_PACK", 3),
        (int)env_i64("KVX_BATCH_PACK", 4)},
-      {env_i64("KVX_WAVE_BYTES_UNPACK", 8 * 1024), (int)env_i64("KVX_NT_UNPACK", 1),
+      {env_i64("KVX_WAVE_BYTES_UNPACK", 8 * 1024), (int)env_i64("KVX_NT_UNPACK", 3),
        (int)env_i64("KVX_BATCH_UNPACK", 8)},
       {env_i64("KVX_WAVE_BYTES_MERGE", 64 * 1024), (int)env_i64("KVX_NT_MERGE", 3),
        (int)env_i64("KVX_BATCH_MERGE", 8)},
       {env_i64("KVX_WAVE_BYTES_SPLIT", 64 * 1024), (int)env_i64("KVX_NT_SPLIT", 3),
        (int)env_i64("KVX_BATCH_SPLIT", 8)},
-      {0, (int)env_i64("KVX_NT_KVF_PACK", 1), (int)env_i64("KVX_BATCH_KVF_PACK", 8)},
-      {0, (int)env_i64("KVX_NT_KVF_UNPACK", 1), (int)env_i64("KVX_BATCH_KVF_UNPACK", 8)},
-      {env_i64("KVX_WAVE_BYTES_DIRECT", 8 * 1024), (int)env_i64("KVX_NT_DIRECT", 1),
+      {0, (int)env_i64("KVX_NT_KVF_PACK", 3), (int)env_i64("KVX_BATCH_KVF_PACK", 8)},
+      {0, (int)env_i64("KVX_NT_KVF_UNPACK", 3), (int)env_i64("KVX_BATCH_KVF_UNPACK", 8)},
+      {env_i64("KVX_WAVE_BYTES_DIRECT", 8 * 1024), (int)env_i64("KVX_NT_DIRECT", 3),
        (int)env_i64("KVX_BATCH_DIRECT", 8)},
       (int)env_i64("KVX_XCD_REMAP", 1),
       (int)env_i64("KVX_XCD_REMAP_SPLIT", 0),
