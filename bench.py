@@ -280,8 +280,8 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step")
 
-    graph_ms = None
-    if not args.no_graph:
+    def graph_replay_ms():
+        """The same step captured once in a HIP graph and replayed: ms per replay."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -297,9 +297,10 @@ def main():
         for _ in range(args.steps):
             g.replay()
         torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        log(f"graph replay: {graph_ms:.4f} ms/step")
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        log(f"graph replay: {ms:.4f} ms/step")
         assert int(err.item()) == 0, "device error flag raised"
+        return ms
 
     copy_bytes = 2 * L * N * BB                    # pack and unpack: each byte read once, written once
     write_bytes = L * R * (2 * 2 * row + 8)        # new-token write: K,V read+write + slot
@@ -377,6 +378,11 @@ def main():
         if not args.no_pipeline:
             out_ops["layer_pipeline"] = layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err,
                                                        max(3, args.op_reps // 2))
+
+    # Captured and replayed after the op timings and the layer pipeline: once a process has
+    # replayed a HIP graph, the pipeline's forward and copy streams overlap worse (the
+    # copy-stream schedule measured 9.48 ms after a replay, 8.56 ms in a process without one).
+    graph_ms = None if args.no_graph else graph_replay_ms()
 
     cpu = None
     if not args.no_cpu_baseline:
