@@ -16,13 +16,14 @@ One step = one pass of the whole hot path over that batch:
 
 Under "ops", each after evicting the Infinity Cache: the same caches under the other
 block-table shape (fragmented tables for the contiguous headline), as kv-first views, the
-direct cache-to-cache copy, the layer-pipelined pack beside a GEMM forward stand-in (with the
-signal as its own launch or inside the pack's), the asymmetric-TP head merge, a plain unpack
-of the same shape and the head split (32 layers, 64 KiB blocks, each on 3 fresh allocations of
-the destination caches), and the 32-request decode
-slot mapping and new-token write (rows of 8 heads, 2 KiB, and of 1 head, 256 B). "cpu_baseline" is the CPU oracle on the whole step.
-"graph_ms_per_step" is the same step captured once in a HIP graph and replayed (`value`
-stays the eager rate: a graph is fixed to one transfer size).
+direct cache-to-cache copy, the layer-pipelined pack beside a GEMM forward stand-in (inline
+or on a copy stream, with the signal as its own launch or inside the pack's), the
+asymmetric-TP head merge, a plain unpack of the same shape and the head split (32 layers,
+64 KiB blocks, each on 3 fresh allocations of the destination caches), and the 32-request
+decode slot mapping and new-token write (rows of 8 heads, 2 KiB, and of 1 head, 256 B).
+"cpu_baseline" is the CPU oracle on the whole step. "graph_ms_per_step" is the same step
+captured once in a HIP graph and replayed, timed after the ops (`value` stays the eager rate:
+a graph is fixed to one transfer size).
 
     python bench.py [--steps K] [--warmup W] [--workload contiguous|fragmented]
                     [--no-cpu-baseline] [--no-ops] [--no-pipeline] [--no-graph] [--copy-calib]
