@@ -19,7 +19,7 @@ block-table shape (fragmented tables for the contiguous headline), as kv-first v
 direct cache-to-cache copy, the layer-pipelined pack beside a GEMM forward stand-in (inline
 or on a copy stream, with the signal as its own launch or inside the pack's), the
 asymmetric-TP head merge, a plain unpack of the same shape and the head split (32 layers,
-64 KiB blocks, each on 3 fresh allocations of the destination caches), and the 32-request
+64 KiB blocks, each on 3 placements of the destination caches in memory), and the 32-request
 decode slot mapping and new-token write (rows of 8 heads, 2 KiB, and of 1 head, 256 B).
 "cpu_baseline" is the CPU oracle on the whole step. "graph_ms_per_step" is the same step
 captured once in a HIP graph and replayed, timed after the ops (`value` stays the eager rate:
@@ -598,9 +598,11 @@ def other_workloads(torch, np, W, K, dev, flush, reps, allocs=3):
     out = {}
     # asymmetric-TP receive: 2 sources x 4 heads -> 8-head caches, 32 layers x 4096 blocks.
     # Rates of this shape move by up to +-10% with the physical pages an allocation lands on
-    # (5.5-6.6 TB/s for the same code in one process), so the destination caches are
-    # allocated afresh `allocs` times and each op reports the median over the allocations of
-    # its median over reps, with every allocation's rate beside it.
+    # (5.3-6.6 TB/s for the same code in one process), so the destination caches are placed
+    # `allocs` times and each op reports the median over the placements of its median over
+    # reps, with every placement's rate beside it. Placement i is allocated while a spacer of
+    # i * 24 GiB is held, so the placements take different regions of memory (a free and a
+    # fresh allocation of the same size can get the same pages back).
     case = W.asym_tp()
     L, N, S = case.dst_spec.num_layers, case.total_blocks, case.num_src
     BB, nb = case.dst_spec.block_bytes, case.dst_spec.num_blocks
@@ -616,7 +618,8 @@ def other_workloads(torch, np, W, K, dev, flush, reps, allocs=3):
     K.kvx_build_xfer_list(ids, None, ro, K.MODE_PACK, xs, cs)
     nbytes = 2 * L * N * BB
     per = {"merge": [], "plain": [], "split": []}
-    for _ in range(allocs):
+    for i in range(allocs):
+        spacer = [torch.empty(1 << 30, dtype=torch.uint8, device=dev) for _ in range(24 * i)]
         dst = [W.fill_device_byte_(torch.empty((nb, BB), dtype=torch.uint8, device=dev)) for _ in range(L)]
         bases = K.layer_base_table(dst)
         for name, fn in (("merge", lambda: K.kvx_unpack(srcs, bases, BB, nb, case.rows_per_block, x, c, N)),
@@ -624,7 +627,7 @@ def other_workloads(torch, np, W, K, dev, flush, reps, allocs=3):
                          ("split", lambda: K.kvx_pack_split(bases, BB, nb, case.rows_per_block, xs, cs, N, srcs))):
             med, _ = time_op(torch, fn, reps, flush)
             per[name].append(med)
-        del dst, bases
+        del dst, bases, spacer
         torch.cuda.empty_cache()
     del srcs, one
     torch.cuda.empty_cache()
@@ -632,10 +635,10 @@ def other_workloads(torch, np, W, K, dev, flush, reps, allocs=3):
     def shape_op(name, workload, counters):
         ms = sorted(per[name])
         med = ms[len(ms) // 2]
-        return {"workload": workload, "bytes": nbytes, "allocations": allocs, "median_ms": round(med, 4),
+        return {"workload": workload, "bytes": nbytes, "placements": allocs, "median_ms": round(med, 4),
                 "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1),
                 "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                "per_allocation_GB/s": [round(nbytes / (t * 1e-3) / 1e9, 1) for t in per[name]],
+                "per_placement_GB/s": [round(nbytes / (t * 1e-3) / 1e9, 1) for t in per[name]],
                 "traffic": traffic_from_counters(counters, nbytes)}
     out["merge_unpack_asym_tp"] = shape_op(
         "merge", "2 sources x 4 of 8 heads, 32 layers x 16 requests x 256 blocks -> [8192][16][K,V][8][128] bf16",
