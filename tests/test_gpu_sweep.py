@@ -15,7 +15,7 @@ from gpu_util import DEV, check_runs_equal, host_bytes, kvx, layers_from_host, l
 
 pytestmark = pytest.mark.gpu
 
-NUM_CASES = 40
+NUM_CASES = 256
 
 
 @pytest.fixture(autouse=True)
