@@ -47,7 +47,7 @@ const Tuning& tuning() {
       (int)env_i64("KVX_XCD_REMAP", 1),
       (int)env_i64("KVX_XCD_REMAP_SPLIT", 0),
       (int)env_i64("KVX_ONE_BATCH", 1),
-      (int)env_i64("KVX_NT_WRITE", 1),
+      (int)env_i64("KVX_NT_WRITE", 0),
       env_i64("KVX_WRITE_VEC_MIN", 4096),
   };
   return t;
@@ -99,9 +99,11 @@ constexpr int kCopyWavesPerWg = kCopyThreads / kWave;
 // 1 KiB wavefront loads a lane issues before its stores (8 -> 8 KiB in flight per wavefront)
 constexpr int kCopyBatch = KVX_COPY_BATCH;
 #ifndef KVX_WRITE_SLOTS
-#define KVX_WRITE_SLOTS 8
+#define KVX_WRITE_SLOTS 4
 #endif
-// 1 KiB slots per wavefront in the new-token write
+// 1 KiB slots per wavefront in the new-token write. 4 against 8: as fast or faster at every
+// row size and token count tried (a shorter chain per wavefront, twice the wavefronts); 2 was
+// within a few percent of 4 either way, 16 slower.
 constexpr int kWriteSlots = KVX_WRITE_SLOTS;
 
 template <bool NT>
@@ -326,8 +328,8 @@ struct WriteArgs {
 };
 
 // New-token write when a row is a multiple of 1 KiB. The (token, K/V, KiB of row) sequence
-// is cut into 1 KiB slots and wavefront w owns slots [8w, 8w + 8): a 2 KiB row puts two
-// tokens in one wavefront, an 8 KiB row spreads a token over two. The row loads do not
+// is cut into 1 KiB slots and wavefront w owns slots [4w, 4w + 4): a 2 KiB row puts one
+// token's K and V in one wavefront, an 8 KiB row spreads a token over four. The row loads do not
 // depend on the slot mapping, so all of them are in flight before the (scalar) slot loads;
 // then each slot's destination is formed and the stores go out, one batch per wavefront.
 template <bool NTL, bool NTS>
@@ -401,9 +403,9 @@ __global__ __launch_bounds__(256) void write_slots_kernel(WriteArgs a) {
   if (bad && lane == 0) raise_error(a.err, KVX_DEVERR_SLOT_RANGE);
 }
 
-// New-token write for rows of up to 4 KiB that are not whole KiB (any multiple of 16 bytes).
+// New-token write for rows of up to 2 KiB that are not whole KiB (any multiple of 16 bytes).
 // A wavefront takes tokens_per_wave whole tokens (as many as fit in kWriteSlots * 64 vectors:
-// 16 tokens of 256-byte rows); lane l of instruction j takes vector 64 j + l of that run of
+// 8 tokens of 256-byte rows); lane l of instruction j takes vector 64 j + l of that run of
 // (token, K/V, 16-byte vector) triples. Each lane's row loads and slot loads are all in flight
 // before its stores. Indexing is by additions from one small division per lane, so a launch
 // of a few tokens costs little more than its memory latency.
