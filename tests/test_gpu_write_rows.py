@@ -1,6 +1,6 @@
 """GPU parity of the new-token write for rows that are not whole KiB, against the oracle.
 Launches of 4096 tokens and more take the vector-sliced kernel (several tokens per
-wavefront, rows up to 4 KiB); smaller launches and longer rows take the one-wavefront-per-token
+wavefront, rows up to 2 KiB); smaller launches and longer rows take the one-wavefront-per-token
 kernel. Cases cover both, rows from 16 B to past 4 KiB, three cache layouts, power-of-two and
 other block sizes, padding tokens, slots past the cache and slots past 2^31."""
 import numpy as np
@@ -66,7 +66,8 @@ def _write_case(seed, T, row, bs, nb, layout, pad_every=0, past_cache=()):
 @pytest.mark.parametrize("row", [16, 48, 128, 256, 400, 1040, 2064, 4080])
 @pytest.mark.parametrize("layout", list(SHAPES))
 def test_vector_kernel_rows(row, layout):
-    """5000 tokens: rows from one vector to 255 vectors (tokens per wavefront 256 down to 1)."""
+    """5000 tokens: rows from one vector to 255 vectors. Up to 2 KiB the vector kernel takes them
+    (tokens per wavefront 128 down to 1); 2064 and 4080 B rows go to the per-token kernel."""
     T, bs = 5000, 16
     nb = -(-T // bs) + 37
     e = _write_case(row * 7 + len(layout), T, row, bs, nb, layout, pad_every=13, past_cache=(5, 4321))
