@@ -10,7 +10,6 @@ import sys
 import numpy as np
 import torch
 
-import oracle as O
 import workloads as W
 
 DEV = "cuda:0"
