@@ -593,9 +593,57 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
     return out
 
 
+def tiny_transfer(torch, np, W, K, dev, iters=200):
+    """The smallest transfer (2 layers, requests of 17, 40 and 5 tokens, 2 KiB blocks, 6 blocks):
+    how long one transfer takes when nothing else is queued, and what each call costs when
+    launches follow each other."""
+    case = W.tiny_roundtrip()
+    spec = case.src_spec
+    L, nb, BB, N = spec.num_layers, spec.num_blocks, spec.block_bytes, case.total_blocks
+    src = [torch.from_numpy(np.ascontiguousarray(c).view(np.uint8).reshape(nb, BB)).to(dev) for c in case.src_caches]
+    dst = [torch.from_numpy(np.ascontiguousarray(c).view(np.uint8).reshape(nb, BB)).to(dev) for c in case.dst_caches]
+    sb, db = K.layer_base_table(src), K.layer_base_table(dst)
+    sid, ro = K.flatten_tables(case.src_tables, dev)
+    did, _ = K.flatten_tables(case.dst_tables, dev)
+    xp, cp = K.new_xfer_list(N, dev)
+    xu, cu = K.new_xfer_list(N, dev)
+    buf = torch.empty(L * N * BB, dtype=torch.uint8, device=dev)
+    calls = {"build_pack": lambda: K.kvx_build_xfer_list(sid, None, ro, K.MODE_PACK, xp, cp),
+             "pack": lambda: K.kvx_pack(sb, BB, nb, xp, cp, N, buf),
+             "build_unpack": lambda: K.kvx_build_xfer_list(None, did, ro, K.MODE_UNPACK, xu, cu),
+             "unpack": lambda: K.kvx_unpack([buf], db, BB, nb, 1, xu, cu, N)}
+
+    def transfer():
+        for fn in calls.values():
+            fn()
+    transfer()
+    torch.cuda.synchronize()
+    lat = []
+    for _ in range(51):  # one transfer on an idle GPU: start event, the four calls, end event
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        transfer()
+        b.record()
+        b.synchronize()
+        lat.append(a.elapsed_time(b) * 1e3)
+    per_call = {}
+    for name, fn in calls.items():  # the same call queued `iters` times in a row
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        b.synchronize()
+        per_call[name] = round(a.elapsed_time(b) * 1e3 / iters, 2)
+    lat.sort()
+    return {"workload": f"{L} layers x {N} blocks of {BB} B (requests of 17, 40 and 5 tokens)",
+            "bytes": 2 * 2 * L * N * BB, "transfer_us_median": round(lat[len(lat) // 2], 2),
+            "transfer_us_min": round(lat[0], 2), "queued_us_per_call": per_call}
+
+
 def other_workloads(torch, np, W, K, dev, flush, reps, allocs=3):
     """The rows the headline batch does not exercise, each on its own workload."""
-    out = {}
+    out = {"tiny_transfer": tiny_transfer(torch, np, W, K, dev)}
     # asymmetric-TP receive: 2 sources x 4 heads -> 8-head caches, 32 layers x 4096 blocks.
     # Rates of this shape move by up to +-10% with the physical pages an allocation lands on
     # (5.3-6.6 TB/s for the same code in one process), so the destination caches are placed
