@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstring>
 #include <mutex>
 
 #include "kvx.h"
@@ -51,7 +52,12 @@ kvx_status scratch_words(hipStream_t stream, uint32_t** out) {
 extern "C" {
 
 const char* kvx_status_string(kvx_status status) {
-  switch (status) {
+  // A C caller may pass any int here. Read the argument's bytes as an int: in C++ a value of
+  // the enum type outside its enumerators has no defined meaning.
+  int32_t code;
+  static_assert(sizeof(code) == sizeof(status), "kvx_status is passed as a 32-bit int");
+  memcpy(&code, &status, sizeof(code));
+  switch (code) {
     case KVX_SUCCESS: return "kvx: success";
     case KVX_ERR_INVALID_ARGUMENT: return "kvx: invalid argument (null pointer, negative size or bad mode)";
     case KVX_ERR_MISALIGNED: return "kvx: pointer, size or stride not a multiple of 16 bytes";
