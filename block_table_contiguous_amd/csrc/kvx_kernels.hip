@@ -569,6 +569,40 @@ __device__ __forceinline__ void chunk_flags(P ro, int32_t R, int64_t N, bool use
   }
 }
 
+// Ids of one prefix round: kPrefixGroups groups of kScanThreads * 4 positions from `base`,
+// 4 consecutive positions per lane (plus the one before and the one after).
+struct PrefixRound {
+  int32_t s[kPrefixGroups][6];
+  int32_t d[kPrefixGroups][6];
+};
+constexpr int64_t kPrefixRound = (int64_t)kScanThreads * 4 * kPrefixGroups;
+
+__device__ __forceinline__ void prefix_load(const int32_t* __restrict__ src,
+                                            const int32_t* __restrict__ dst, int64_t N,
+                                            bool use_src, bool use_dst, int64_t base,
+                                            PrefixRound& r) {
+#pragma unroll
+  for (int g = 0; g < kPrefixGroups; ++g)
+    chunk_ids<4>(src, dst, N, use_src, use_dst, base + ((int64_t)g * kScanThreads + threadIdx.x) * 4,
+                 r.s[g], r.d[g]);
+}
+
+// Id breaks among the round's positions that lie in [1, begin): count and latest position.
+__device__ __forceinline__ void prefix_count(const PrefixRound& r, int64_t base, int64_t begin,
+                                             bool use_src, bool use_dst, int64_t& pc, int64_t& pl) {
+#pragma unroll
+  for (int g = 0; g < kPrefixGroups; ++g) {
+    const int64_t q0 = base + ((int64_t)g * kScanThreads + threadIdx.x) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t p = q0 + i;
+      const bool brk = (use_src && (int64_t)r.s[g][i + 1] != (int64_t)r.s[g][i] + 1) ||
+                       (use_dst && (int64_t)r.d[g][i + 1] != (int64_t)r.d[g][i] + 1);
+      if (p >= 1 && p < begin && brk) { ++pc; pl = p; }
+    }
+  }
+}
+
 // Workgroup b owns positions [b * span, (b + 1) * span), span a multiple of kScanTile. It
 // first counts the run starts before its range and finds the latest of them (a pass over
 // every earlier id and over the request offsets, no writes). Then, one kScanTile sub-tile
@@ -576,13 +610,21 @@ __device__ __forceinline__ void chunk_flags(P ro, int32_t R, int64_t N, bool use
 // latest-start positions with a wave scan plus a 4-entry LDS pass, and writes the runs each
 // thread starts and the lengths of the runs it ends, carrying the count and the latest start
 // to the next sub-tile. No thread reads another's output, and no workgroup waits for another.
-// Request offsets are staged in LDS when there are fewer than kLdsOffsets requests.
+//
+// The kernel is a chain of dependent memory round trips, so every load that depends on
+// nothing is issued at the start, before the request offsets are staged in LDS: the ids of
+// the first sub-tile, the first prefix round and, with fewer than kScanThreads requests, one
+// offset per thread. The ids at the request starts (which need the offsets) are loaded before
+// the prefix pass's arithmetic, and each later sub-tile's or round's ids before the current
+// one is scanned.
 template <class P>
 __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
                                            const int32_t* __restrict__ dst, P ro, int32_t R,
                                            int64_t N, bool use_src, bool use_dst,
                                            kvx_xfer* __restrict__ out, int64_t* __restrict__ count,
-                                           int64_t span, int64_t* s_cnt, int64_t* s_last) {
+                                           int64_t span, int64_t* s_cnt, int64_t* s_last,
+                                           int32_t (&sv)[kScanItems + 2], int32_t (&dv)[kScanItems + 2],
+                                           PrefixRound& cur) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;
@@ -592,35 +634,48 @@ __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
   // 1. run starts before the range: count and latest position. With a valid CSR a position
   //    p in [1, begin) starts a run iff its ids break the +1 step from p - 1 or a request
   //    starts at p, so the count is: position 0, plus the id breaks, plus the request starts
-  //    that are not id breaks. (a) streams the ids in rounds of kPrefixGroups groups of
-  //    kScanThreads * 4 positions, 4 consecutive positions per lane; (b) walks the offsets.
+  //    that are not id breaks. (b) finds the request starts in [1, begin) (the first request
+  //    at each) and loads the ids on both sides of each; (a) streams the ids in rounds.
   int64_t pc = 0, pl = -1;
+  const bool one_each = R < kScanThreads;
   if (begin > 0) {
-    for (int64_t base = 0; base < begin; base += (int64_t)kScanThreads * 4 * kPrefixGroups) {
-      int32_t sv[kPrefixGroups][6], dv[kPrefixGroups][6];
-#pragma unroll
-      for (int g = 0; g < kPrefixGroups; ++g)
-        chunk_ids<4>(src, dst, N, use_src, use_dst, base + ((int64_t)g * kScanThreads + tid) * 4,
-                     sv[g], dv[g]);
-#pragma unroll
-      for (int g = 0; g < kPrefixGroups; ++g) {
-        const int64_t q0 = base + ((int64_t)g * kScanThreads + tid) * 4;  // never straddles the range
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t p = q0 + i;
-          const bool brk = (use_src && (int64_t)sv[g][i + 1] != (int64_t)sv[g][i] + 1) ||
-                           (use_dst && (int64_t)dv[g][i + 1] != (int64_t)dv[g][i] + 1);
-          if (p >= 1 && p < begin && brk) { ++pc; pl = p; }
-        }
+    // with fewer than kScanThreads requests, thread t takes request 1 + t: its start and the
+    // ids on both sides of it are loaded before (a) runs
+    const int32_t r1 = 1 + tid;
+    int64_t q = 0;
+    bool qs = false;
+    int32_t a0 = 0, a1 = 0, b0 = 0, b1 = 0;
+    if (one_each && r1 < R) {
+      q = ro[r1];
+      qs = q >= 1 && q < begin && q != ro[r1 - 1];  // the first request starting at q
+      if (qs) {
+        if (use_src) { a0 = src[q - 1]; a1 = src[q]; }
+        if (use_dst) { b0 = dst[q - 1]; b1 = dst[q]; }
       }
     }
-    for (int32_t r = 1 + tid; r < R; r += kScanThreads) {
-      const int64_t q = ro[r];
-      if (q >= 1 && q < begin && q != ro[r - 1]) {  // the first request starting at q
+    for (int64_t base = 0; base < begin; base += kPrefixRound) {
+      const bool more = base + kPrefixRound < begin;
+      PrefixRound nxt;
+      if (more) prefix_load(src, dst, N, use_src, use_dst, base + kPrefixRound, nxt);
+      prefix_count(cur, base, begin, use_src, use_dst, pc, pl);
+      if (more) cur = nxt;
+    }
+    if (one_each) {
+      if (qs) {
         pl = q > pl ? q : pl;
-        const bool brk = (use_src && (int64_t)src[q] != (int64_t)src[q - 1] + 1) ||
-                         (use_dst && (int64_t)dst[q] != (int64_t)dst[q - 1] + 1);
+        const bool brk = (use_src && (int64_t)a1 != (int64_t)a0 + 1) ||
+                         (use_dst && (int64_t)b1 != (int64_t)b0 + 1);
         if (!brk) ++pc;
+      }
+    } else {
+      for (int32_t r = 1 + tid; r < R; r += kScanThreads) {
+        const int64_t qr = ro[r];
+        if (qr >= 1 && qr < begin && qr != ro[r - 1]) {  // the first request starting at qr
+          pl = qr > pl ? qr : pl;
+          const bool brk = (use_src && (int64_t)src[qr] != (int64_t)src[qr - 1] + 1) ||
+                           (use_dst && (int64_t)dst[qr] != (int64_t)dst[qr - 1] + 1);
+          if (!brk) ++pc;
+        }
       }
     }
     if (tid == 0) {  // position 0
@@ -644,12 +699,14 @@ __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
   }
   __syncthreads();
 
-  // 2. the own range, one sub-tile at a time
+  // 2. the own range, one sub-tile at a time (sv / dv hold the current sub-tile's ids)
   for (int64_t tile = begin; tile < end; tile += kScanTile) {
     const int64_t p0 = tile + (int64_t)tid * kScanItems;
+    const bool more = tile + kScanTile < end;
+    int32_t nsv[kScanItems + 2], ndv[kScanItems + 2];
+    if (more) chunk_ids<kScanItems>(src, dst, N, use_src, use_dst, p0 + kScanTile, nsv, ndv);
     bool st[kScanItems + 1];
-    int32_t rq[kScanItems], sv[kScanItems + 2], dv[kScanItems + 2];
-    if (N > 0) chunk_ids<kScanItems>(src, dst, N, use_src, use_dst, p0, sv, dv);
+    int32_t rq[kScanItems];
     chunk_flags<kScanItems>(ro, R, N, use_src, use_dst, p0, sv, dv, st, rq);
     int64_t cnt = 0, last = -1;
 #pragma unroll
@@ -678,9 +735,9 @@ __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
     }
 
     int64_t k = carry_cnt + c_before + (ci - cnt);
-    int64_t cur = carry_last;
-    if (l_before > cur) cur = l_before;
-    if (li_excl > cur) cur = li_excl;
+    int64_t cur_start = carry_last;
+    if (l_before > cur_start) cur_start = l_before;
+    if (li_excl > cur_start) cur_start = li_excl;
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
       const int64_t p = p0 + i;
@@ -704,15 +761,19 @@ __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
             out[k].buf_block = p;
             out[k].req = rq[i];
           }
-          cur = p;
+          cur_start = p;
           ++k;
         } else if (ends) {
-          out[k - 1].num_blocks = (int32_t)(p - cur + 1);
+          out[k - 1].num_blocks = (int32_t)(p - cur_start + 1);
         }
       }
     }
     carry_cnt += c_tile;
     if (l_tile > carry_last) carry_last = l_tile;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < kScanItems + 2; ++i) { sv[i] = nsv[i]; dv[i] = ndv[i]; }
+    }
     __syncthreads();  // the next sub-tile reuses s_cnt / s_last
   }
   if (blockIdx.x == gridDim.x - 1 && tid == 0) *count = carry_cnt;
@@ -729,22 +790,41 @@ __global__ __launch_bounds__(kScanThreads) void build_xfer_kernel(
   const bool use_src = mode != KVX_MODE_UNPACK;
   const bool use_dst = mode != KVX_MODE_PACK;
   const bool in_lds = R < kLdsOffsets;
-  const bool check = blockIdx.x == 0;  // one workgroup checks the CSR
+  const bool one_each = R < kScanThreads;  // at most one offset per thread
+  const bool check = blockIdx.x == 0;      // one workgroup checks the CSR
+  const int64_t begin = (int64_t)blockIdx.x * span;
 
-  // CSR sanity: ro[0] == 0, non-decreasing, ro[R] == N
-  if (in_lds || check) {
+  // loads that depend on nothing, in flight together
+  int64_t my_ro = 0;
+  if (one_each && tid <= R) my_ro = ro[tid];
+  int32_t sv[kScanItems + 2], dv[kScanItems + 2];
+  if (N > 0) chunk_ids<kScanItems>(src, dst, N, use_src, use_dst, begin + (int64_t)tid * kScanItems, sv, dv);
+  PrefixRound cur;
+  if (begin > 0) prefix_load(src, dst, N, use_src, use_dst, 0, cur);
+
+  // stage the offsets in LDS; CSR sanity: ro[0] == 0, non-decreasing, ro[R] == N
+  if (one_each) {
+    if (tid <= R) s_ro[tid] = my_ro;
+  } else if (in_lds || check) {
     for (int32_t i = tid; i <= R; i += kScanThreads) {
       const int64_t v = ro[i];
       if (in_lds) s_ro[i] = v;
       if (check && i < R && ro[i + 1] < v) raise_error(err, KVX_DEVERR_OFFSETS);
     }
   }
-  if (check && tid == 0 && (ro[0] != 0 || ro[R] != N)) raise_error(err, KVX_DEVERR_OFFSETS);
   __syncthreads();
+  if (check) {
+    if (one_each) {
+      if (tid < R && s_ro[tid + 1] < s_ro[tid]) raise_error(err, KVX_DEVERR_OFFSETS);
+      if (tid == 0 && (s_ro[0] != 0 || s_ro[R] != N)) raise_error(err, KVX_DEVERR_OFFSETS);
+    } else if (tid == 0 && (ro[0] != 0 || ro[R] != N)) {
+      raise_error(err, KVX_DEVERR_OFFSETS);
+    }
+  }
   if (in_lds)
-    build_tile<const int64_t*>(src, dst, s_ro, R, N, use_src, use_dst, out, count, span, s_cnt, s_last);
+    build_tile<const int64_t*>(src, dst, s_ro, R, N, use_src, use_dst, out, count, span, s_cnt, s_last, sv, dv, cur);
   else
-    build_tile<const int64_t*>(src, dst, ro, R, N, use_src, use_dst, out, count, span, s_cnt, s_last);
+    build_tile<const int64_t*>(src, dst, ro, R, N, use_src, use_dst, out, count, span, s_cnt, s_last, sv, dv, cur);
 }
 
 // --------------------------------------------------------------------------------------

@@ -148,6 +148,35 @@ def test_offsets_beyond_the_lds_stage():
     run_case(case)
 
 
+@pytest.mark.parametrize("num_reqs,max_len,seed", [(8, 6000, 93), (200, 7000, 94), (255, 7000, 95),
+                                                   (256, 7000, 96)])
+def test_run_lists_few_requests_many_positions(num_reqs, max_len, seed):
+    """Run lists in every mode from a few hundred requests or fewer over many positions of
+    16-byte blocks: the builder's prefix pass takes several rounds, and past 524,288 positions
+    each workgroup walks several sub-tiles. Up to 255 requests each builder thread handles one
+    request start; 256 take the general path. Every fifth request is empty."""
+    rng = np.random.default_rng(seed)
+    lengths = [int(x) for x in rng.integers(1, max_len, size=num_reqs)]
+    for i in range(0, num_reqs, 5):
+        lengths[i] = 0
+    case = W.random_transfer(seed, 1, 2_000_000, 1, 1, 8, lengths, elem_bytes=1, with_caches=False)
+    if num_reqs > 8:
+        assert case.total_blocks > 256 * 2048
+    else:
+        assert case.total_blocks > 4 * 4096
+    K = kvx()
+    sid, ro = K.flatten_tables(case.src_tables, DEV)
+    did, _ = K.flatten_tables(case.dst_tables, DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for mode, omode, a, b in ((K.MODE_PACK, O.MODE_PACK, sid, None),
+                              (K.MODE_UNPACK, O.MODE_UNPACK, None, did),
+                              (K.MODE_DIRECT, O.MODE_DIRECT, sid, did)):
+        x, c = K.new_xfer_list(case.total_blocks, DEV)
+        K.kvx_build_xfer_list(a, b, ro, mode, x, c, err)
+        check_runs_equal(K, x, c, O.xfer_list(case.src_tables, case.dst_tables, omode))
+    assert int(err.item()) == 0
+
+
 def test_single_request_single_block():
     run_case(W.random_transfer(5, 1, 16, 16, 1, 8, [3]))
 
