@@ -553,20 +553,68 @@ __device__ __forceinline__ void chunk_flags(P ro, int32_t R, int64_t N, bool use
                                             const int32_t (&sv)[ITEMS + 2],
                                             const int32_t (&dv)[ITEMS + 2],
                                             bool (&st)[ITEMS + 1], int32_t (&rq)[ITEMS]) {
+  // r is the request holding p; cur and nxt are the starts of r and of r + 1 (past the last
+  // request, never reached), kept in registers so that LDS is read again only where a request
+  // boundary falls among the chunk's positions
+  constexpr int64_t kNever = INT64_MAX;
   int32_t r = (p0 < N) ? find_request(ro, R, p0) : 0;
+  int64_t cur = ro[r];
+  int64_t nxt = r + 1 < R ? ro[r + 1] : kNever;
 #pragma unroll
   for (int i = 0; i <= ITEMS; ++i) {
     const int64_t p = p0 + i;
     bool f = false;
     if (p < N) {
-      while (r + 1 < R && ro[r + 1] <= p) ++r;
-      f = (p == 0) || (p == ro[r]) ||
+      while (nxt <= p) {
+        ++r;
+        cur = nxt;
+        nxt = r + 1 < R ? ro[r + 1] : kNever;
+      }
+      f = (p == 0) || (p == cur) ||
           (use_src && (int64_t)sv[i + 1] != (int64_t)sv[i] + 1) ||
           (use_dst && (int64_t)dv[i + 1] != (int64_t)dv[i] + 1);
     }
     st[i] = f;
     if (i < ITEMS) rq[i] = r;
   }
+}
+
+// Wave-wide inclusive scans of 32-bit values with DPP moves: row shifts by 1, 2, 4 and 8
+// inside each row of 16 lanes, then the broadcasts of lane 15 into rows 1 and 3 and of lane 31
+// into rows 2 and 3. A lane whose source lies outside its row, or whose row the mask leaves
+// out, takes the identity. Each step is a register move between lanes, where a shuffle would
+// be a round trip through the LDS crossbar.
+constexpr int kDppRowShr = 0x110, kDppWaveShr1 = 0x138, kDppRowBcast15 = 0x142,
+              kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int32_t dpp_move(int32_t identity, int32_t v) {
+  return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROWS, 0xf, false);
+}
+
+__device__ __forceinline__ int32_t wave_scan_sum(int32_t v) {
+  v += dpp_move<kDppRowShr + 1, 0xf>(0, v);
+  v += dpp_move<kDppRowShr + 2, 0xf>(0, v);
+  v += dpp_move<kDppRowShr + 4, 0xf>(0, v);
+  v += dpp_move<kDppRowShr + 8, 0xf>(0, v);
+  v += dpp_move<kDppRowBcast15, 0xa>(0, v);
+  v += dpp_move<kDppRowBcast31, 0xc>(0, v);
+  return v;
+}
+
+__device__ __forceinline__ int32_t wave_scan_max(int32_t v) {
+  v = max(v, dpp_move<kDppRowShr + 1, 0xf>(INT32_MIN, v));
+  v = max(v, dpp_move<kDppRowShr + 2, 0xf>(INT32_MIN, v));
+  v = max(v, dpp_move<kDppRowShr + 4, 0xf>(INT32_MIN, v));
+  v = max(v, dpp_move<kDppRowShr + 8, 0xf>(INT32_MIN, v));
+  v = max(v, dpp_move<kDppRowBcast15, 0xa>(INT32_MIN, v));
+  v = max(v, dpp_move<kDppRowBcast31, 0xc>(INT32_MIN, v));
+  return v;
+}
+
+// v of the lane before across the whole wave; `first` in lane 0
+__device__ __forceinline__ int32_t wave_shift_up(int32_t v, int32_t first) {
+  return dpp_move<kDppWaveShr1, 0xf>(first, v);
 }
 
 // Ids of one prefix round: kPrefixGroups groups of kScanThreads * 4 positions from `base`,
@@ -683,13 +731,19 @@ __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
       pl = pl > 0 ? pl : 0;
     }
   }
+  if (N <= INT32_MAX) {  // counts and positions fit 32 bits: DPP scans, totals in the last lane
+    const int32_t c = wave_scan_sum((int32_t)pc);
+    const int32_t l = wave_scan_max((int32_t)pl);
+    if (lane == kWave - 1) { s_cnt[wid] = c; s_last[wid] = l; }
+  } else {
 #pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    pc += __shfl_xor(pc, d, kWave);
-    const int64_t o = __shfl_xor(pl, d, kWave);
-    pl = o > pl ? o : pl;
+    for (int d = 1; d < kWave; d <<= 1) {
+      pc += __shfl_xor(pc, d, kWave);
+      const int64_t o = __shfl_xor(pl, d, kWave);
+      pl = o > pl ? o : pl;
+    }
+    if (lane == 0) { s_cnt[wid] = pc; s_last[wid] = pl; }
   }
-  if (lane == 0) { s_cnt[wid] = pc; s_last[wid] = pl; }
   __syncthreads();
   int64_t carry_cnt = 0, carry_last = -1;
 #pragma unroll
@@ -713,16 +767,14 @@ __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
     for (int i = 0; i < kScanItems; ++i)
       if (st[i]) { ++cnt; last = p0 + i; }
 
-    // workgroup scan of (cnt: sum, last: max)
-    int64_t ci = cnt, li = last;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int64_t c = __shfl_up(ci, d, kWave);
-      const int64_t l = __shfl_up(li, d, kWave);
-      if (lane >= d) { ci += c; li = l > li ? l : li; }
-    }
-    int64_t li_excl = __shfl_up(li, 1, kWave);
-    if (lane == 0) li_excl = -1;
+    // workgroup scan of (cnt: sum, last: max): wave scans in 32 bits with the latest start
+    // relative to the sub-tile, then a 4-entry LDS pass
+    const int32_t ci32 = wave_scan_sum((int32_t)cnt);
+    const int32_t li32 = wave_scan_max(last < 0 ? -1 : (int32_t)(last - tile));
+    const int32_t lx32 = wave_shift_up(li32, -1);  // li of the lane before, -1 in lane 0
+    const int64_t ci = ci32;
+    const int64_t li = li32 < 0 ? -1 : tile + li32;
+    const int64_t li_excl = lx32 < 0 ? -1 : tile + lx32;
     if (lane == kWave - 1) { s_cnt[wid] = ci; s_last[wid] = li; }
     __syncthreads();
     int64_t c_before = 0, l_before = -1, c_tile = 0, l_tile = -1;
@@ -763,7 +815,7 @@ __device__ __forceinline__ void build_tile(const int32_t* __restrict__ src,
           }
           cur_start = p;
           ++k;
-        } else if (ends) {
+        } else if (ends && k > 0) {  // k > 0 always: position 0 starts a run
           out[k - 1].num_blocks = (int32_t)(p - cur_start + 1);
         }
       }
