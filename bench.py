@@ -21,7 +21,9 @@ direct cache-to-cache copy, the layer-pipelined pack beside a GEMM forward stand
 or on a copy stream, with the signal as its own launch or inside the pack's), the
 asymmetric-TP head merge, a plain unpack of the same shape and the head split (32 layers,
 64 KiB blocks, each on 3 placements of the destination caches in memory), and the 32-request
-decode slot mapping and new-token write (rows of 8 heads, 2 KiB, and of 1 head, 256 B).
+decode slot mapping and new-token write (rows of 8 heads, 2 KiB, and of 1 head, 256 B). The
+smallest transfer (2 layers, 6 blocks of 2 KiB) is timed on an idle GPU, as calls queued back
+to back (beside the host's time to issue them) and replayed from a HIP graph.
 "cpu_baseline" is the CPU oracle on the whole step. "graph_ms_per_step" is the same step
 captured once in a HIP graph and replayed, timed after the ops (`value` stays the eager rate:
 a graph is fixed to one transfer size).
@@ -604,8 +606,9 @@ def layer_pipeline(torch, K, dev, L, nb, BB, N, src_bases, buf, xp, cp, err, rep
 
 def tiny_transfer(torch, np, W, K, dev, iters=200):
     """The smallest transfer (2 layers, requests of 17, 40 and 5 tokens, 2 KiB blocks, 6 blocks):
-    how long one transfer takes when nothing else is queued, and what each call costs when
-    launches follow each other."""
+    how long one transfer takes when nothing else is queued, what each call costs when launches
+    follow each other (with the host time the Python calls take to enqueue them), and how long
+    the transfer takes replayed from a HIP graph, with no host work between its kernels."""
     case = W.tiny_roundtrip()
     spec = case.src_spec
     L, nb, BB, N = spec.num_layers, spec.num_blocks, spec.block_bytes, case.total_blocks
@@ -635,19 +638,49 @@ def tiny_transfer(torch, np, W, K, dev, iters=200):
         b.record()
         b.synchronize()
         lat.append(a.elapsed_time(b) * 1e3)
-    per_call = {}
+    per_call, host_per_call = {}, {}
     for name, fn in calls.items():  # the same call queued `iters` times in a row
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
+        t0 = time.perf_counter()
         for _ in range(iters):
             fn()
+        host_per_call[name] = round((time.perf_counter() - t0) * 1e6 / iters, 2)
         b.record()
         b.synchronize()
         per_call[name] = round(a.elapsed_time(b) * 1e3 / iters, 2)
     lat.sort()
+    # The four calls captured once in a HIP graph and replayed: one transfer with no host work
+    # (Python, argument checks, launch calls) between its kernels. Each replay must leave the
+    # same bytes as the eager transfer.
+    want_buf, want_dst = buf.clone(), [t.clone() for t in dst]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        transfer()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        transfer()
+    g.replay()
+    torch.cuda.synchronize()
+    glat = []
+    for _ in range(51):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        glat.append(a.elapsed_time(b) * 1e3)
+    assert torch.equal(buf, want_buf) and all(torch.equal(t, w) for t, w in zip(dst, want_dst)), \
+        "graph-replayed tiny transfer differs from the eager one"
+    glat.sort()
     return {"workload": f"{L} layers x {N} blocks of {BB} B (requests of 17, 40 and 5 tokens)",
             "bytes": 2 * 2 * L * N * BB, "transfer_us_median": round(lat[len(lat) // 2], 2),
-            "transfer_us_min": round(lat[0], 2), "queued_us_per_call": per_call}
+            "transfer_us_min": round(lat[0], 2), "queued_us_per_call": per_call,
+            "host_us_per_call": host_per_call,
+            "graph_transfer_us_median": round(glat[len(glat) // 2], 2),
+            "graph_transfer_us_min": round(glat[0], 2)}
 
 
 def other_workloads(torch, np, W, K, dev, flush, reps, allocs=3):
