@@ -11,7 +11,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_util import log
+from gpu_util import kvx, log
 
 pytestmark = pytest.mark.gpu
 
@@ -87,9 +87,10 @@ REST_MAGIC = 0x4B565852
 
 def test_plain_c_rest_of_the_abi(tmp_path):
     """tests/c_abi/rest.c: the slot mapping and new-token write, the kv-first pack and unpack,
-    the head split and the two-source merge, the signal add and wait, and the signalling pack
-    feeding a consumer stream layer by layer, all from plain C; every output against the
-    oracle, and eight host-side status codes."""
+    the head split and the two-source merge, the signal add and wait, the signalling pack and
+    the signalling direct copy each feeding a consumer stream layer by layer, the
+    allocation-free signalling pack likewise, and the ABI version, all from plain C; every
+    output against the oracle, and ten host-side status codes."""
     assert os.path.exists(REST), "tests/c_abi/rest is built by __graft_entry__.build()"
     rng = np.random.default_rng(77)
     bs, H, D, L, nb = 16, 1, 64, 2, 200
@@ -131,8 +132,8 @@ def test_plain_c_rest_of_the_abi(tmp_path):
     log(r.stdout.strip())
     assert r.returncode == 0, r.stderr
     raw = np.fromfile(out, np.uint8)
-    hdr = raw[:40].view(np.int64)
-    at = 40
+    hdr = raw[:64].view(np.int64)
+    at = 64
 
     def take(n):
         nonlocal at
@@ -147,11 +148,16 @@ def test_plain_c_rest_of_the_abi(tmp_path):
     sh0, sh1 = take(L * N * BB // 2), take(L * N * BB // 2)
     merged = take(L * nb * BB).reshape(L, nb, BB)
     signalled = take(L * nb * BB).reshape(L, nb, BB)
+    seen = take(L * nb * BB).reshape(L, nb, BB)
+    nbuf = take(L * N * BB)
+    nsignalled = take(L * nb * BB).reshape(L, nb, BB)
     assert at == raw.size
 
     assert int(hdr[0]) == 0 and int(hdr[1]) == 0, "error flags"
     assert int(hdr[2]) == L and int(hdr[3]) == 42, "signal counters"
-    assert int(hdr[4]) == 8, "host-side status checks"
+    assert int(hdr[4]) == 10, "host-side status checks"
+    assert int(hdr[5]) == kvx().kvx_abi_version(), "ABI version"
+    assert int(hdr[6]) == L and int(hdr[7]) == L, "direct-copy and allocation-free signal counters"
     exp_slots, e = O.slot_mapping(table, req, pos, bs)
     assert e == 0 and np.array_equal(slots, exp_slots)
     exp_w, e = O.reshape_and_cache(dst[0], key, val, exp_slots, nb, bs, bs * 2 * row, 2 * row, row)
@@ -166,7 +172,12 @@ def test_plain_c_rest_of_the_abi(tmp_path):
     exp_buf, e1 = O.pack(src, case.src_tables)
     exp_s, e2 = O.unpack([exp_buf], dst, case.dst_tables)
     assert e1 == e2 == 0
+    exp_d, e = O.copy_direct(src, dst, case.src_tables, case.dst_tables)
+    assert e == 0
+    assert np.array_equal(nbuf, exp_buf.reshape(-1)), "allocation-free signalled pack"
     for l in range(L):
         assert np.array_equal(kvf[l], exp_kvf[l].reshape(nb, BB)), f"kv-first layer {l}"
         assert np.array_equal(merged[l], exp_m[l]), f"merge layer {l}"
         assert np.array_equal(signalled[l], exp_s[l]), f"signalled transfer layer {l}"
+        assert np.array_equal(seen[l], exp_d[l]), f"direct layer {l} as seen after its signal"
+        assert np.array_equal(nsignalled[l], exp_s[l]), f"allocation-free signalled transfer layer {l}"
