@@ -331,6 +331,8 @@ def main():
         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
         "traffic": traffic_from_counters(f"{dominant}_{case.name}", copy_bytes),
         "algorithmic_bytes": copy_bytes, "avg_launch_ms": round(kern[dominant], 5),
+        "events": "HIP events around each kernel on its stream, over a second run of the same "
+                  "K steps (evented_ms_per_step); the headline steps carry none",
     }
     out_ops = {n: {"avg_ms": round(v, 5)} for n, v in kern.items()}
     for n in ("pack", "unpack"):
