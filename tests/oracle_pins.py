@@ -41,6 +41,20 @@ def pin_slot_golden(o):
         assert err == case.get("expected_err", 0), case["name"]
 
 
+def pin_slot_outside_the_table(o):
+    """Reading R10 on a table with no padding (so an index taken from the wrong end of a row
+    would land on a real block): a token whose request index is past the table or negative,
+    or whose position is negative or past its row, gets slot -1 and the table-range bit; the
+    in-range tokens beside them keep their slots by the slot rule."""
+    bt = np.array([[5, 7], [2, 9]], np.int32)
+    bs = 4
+    req = [0, 0, 1, 2, -1, 0, 1]
+    pos = [3, -1, 5, 0, 0, 8, 7]
+    slots, err = o.slot_mapping(bt, req, pos, bs)
+    assert slots.tolist() == [5 * 4 + 3, -1, 9 * 4 + 1, -1, -1, -1, 9 * 4 + 3]
+    assert err == o.DEVERR_TABLE_RANGE
+
+
 def pin_slot_owner_brute_force(o):
     """Walk every slot of every listed block and record which (request, position) owns it;
     each token's slot must be owned by that token."""

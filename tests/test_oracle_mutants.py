@@ -66,6 +66,12 @@ MUTANTS = [
     ("unpack_repeats_out_of_cache_rejected", "order if 0 <= int(dst_tables[r][j]) < nb]", "order]"),
     ("direct_repeats_out_of_cache_rejected", "for d in t if 0 <= int(d) < nbd]", "for d in t]"),
     ("kv_first_repeats_out_of_cache_rejected", "for d in t if 0 <= int(d) < nb]", "for d in t]"),
+    ("slot_request_past_table", "if r < 0 or r >= num_reqs or pos < 0", "if r < 0 or pos < 0"),
+    ("slot_negative_position", "if r < 0 or r >= num_reqs or pos < 0 or", "if r < 0 or r >= num_reqs or"),
+    ("reshape_value_over_key", "out[at + kv_stride:at + kv_stride + row] = V[i]", "out[at:at + row] = V[i]"),
+    ("reshape_block_stride_as_token", "at = block * block_stride + offset * token_stride",
+     "at = block * token_stride + offset * token_stride"),
+    ("direct_no_src_lower_check", "if s < 0 or s >= nbs or d < 0 or d >= nbd:", "if s >= nbs or d < 0 or d >= nbd:"),
 ]
 
 
