@@ -42,10 +42,11 @@ def pin_slot_golden(o):
 
 
 def pin_slot_outside_the_table(o):
-    """Reading R10 on a table with no padding (so an index taken from the wrong end of a row
-    would land on a real block): a token whose request index is past the table or negative,
-    or whose position is negative or past its row, gets slot -1 and the table-range bit; the
-    in-range tokens beside them keep their slots by the slot rule."""
+    """Tokens the slot rule cannot place (the pages define only the in-range case; the reading
+    taken is slot -1 and the table-range bit), on a table with no padding, so that an index
+    taken from the wrong end of a row would land on a real block: a request index past the
+    table or negative, a position negative or past its row. The in-range tokens beside them
+    keep their slots by the slot rule."""
     bt = np.array([[5, 7], [2, 9]], np.int32)
     bs = 4
     req = [0, 0, 1, 2, -1, 0, 1]
