@@ -163,6 +163,8 @@ def _stream(stream) -> Optional[int]:
 
 def _rows_contiguous(t) -> bool:
     """Every t[i] is densely packed (the dimensions after the first are contiguous)."""
+    if t.is_contiguous():  # the common case, without walking the strides
+        return True
     expect = 1
     for size, stride in zip(reversed(t.shape[1:]), reversed(t.stride()[1:])):
         if size != 1 and stride != expect:
