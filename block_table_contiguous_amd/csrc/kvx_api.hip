@@ -26,6 +26,20 @@ inline kvx_status from_hip(hipError_t e) { return e == hipSuccess ? KVX_SUCCESS 
 
 constexpr int64_t kMaxBlocks = 0x7fffffff;  // block ids and run lengths are int32
 
+// count x bytes stays within KVX_MAX_EXTENT_BYTES (both non-negative): the kernels form 64-bit
+// byte offsets from such products, and nothing larger can be a real allocation.
+inline bool extent_ok(int64_t count, int64_t bytes) {
+  return count >= 0 && bytes >= 0 && (count == 0 || bytes <= KVX_MAX_EXTENT_BYTES / count);
+}
+
+// A copy's extents: one layer's cache (blocks x block bytes) and the whole buffer or transfer
+// (layers x blocks x block bytes; layers and blocks are both below 2^31, so their product fits).
+inline bool copy_extents_ok(int32_t num_layers, int64_t total_blocks, int64_t cache_blocks,
+                            int64_t block_bytes) {
+  return extent_ok(cache_blocks, block_bytes) &&
+         extent_ok((int64_t)num_layers * total_blocks, block_bytes);
+}
+
 // Device address of `scratch` on the GPU that owns `stream`, looked up once per device (with
 // that device current: the call requires it) and kept. No allocation is involved.
 constexpr int kMaxDevices = 64;
@@ -75,7 +89,8 @@ kvx_status kvx_slot_mapping(const int32_t* block_table, int64_t num_reqs,
                             int64_t num_tokens, int32_t block_size, int64_t* slot_mapping,
                             int32_t* err_flag, hipStream_t stream) {
   if (num_tokens < 0 || num_reqs < 0 || block_size < 1 || max_blocks_per_req < 0 ||
-      bt_row_stride < max_blocks_per_req)
+      bt_row_stride < max_blocks_per_req || !extent_ok(num_reqs, bt_row_stride) ||
+      !extent_ok(num_tokens, 8))
     return KVX_ERR_INVALID_ARGUMENT;
   if (num_tokens == 0) return KVX_SUCCESS;
   if (!req_idx || !positions || !slot_mapping || (num_reqs > 0 && !block_table))
@@ -95,6 +110,10 @@ kvx_status kvx_reshape_and_cache(const void* key, int64_t key_stride_bytes, cons
   if (num_tokens < 0 || row_bytes <= 0 || num_blocks < 0 || block_size < 1 ||
       key_stride_bytes < 0 || value_stride_bytes < 0 || block_stride_bytes < 0 ||
       token_stride_bytes < 0 || kv_stride_bytes < 0)
+    return KVX_ERR_INVALID_ARGUMENT;
+  if (!extent_ok(num_blocks, block_stride_bytes) || !extent_ok(block_size, token_stride_bytes) ||
+      !extent_ok(num_tokens, key_stride_bytes) || !extent_ok(num_tokens, value_stride_bytes) ||
+      !extent_ok(1, kv_stride_bytes) || !extent_ok(num_tokens, row_bytes))
     return KVX_ERR_INVALID_ARGUMENT;
   if (num_tokens == 0) return KVX_SUCCESS;
   if (!key || !value || !slot_mapping || !kv_cache) return KVX_ERR_INVALID_ARGUMENT;
@@ -135,7 +154,8 @@ kvx_status kvx_pack(void* const* layer_bases, int32_t num_layers, int64_t block_
                     const int64_t* xfer_count, int64_t total_blocks, void* send_buf,
                     int32_t* err_flag, hipStream_t stream) {
   if (num_layers < 0 || block_bytes <= 0 || num_cache_blocks < 0 || total_blocks < 0 ||
-      total_blocks > kMaxBlocks)
+      total_blocks > kMaxBlocks ||
+      !copy_extents_ok(num_layers, total_blocks, num_cache_blocks, block_bytes))
     return KVX_ERR_INVALID_ARGUMENT;
   if (num_layers == 0 || total_blocks == 0) return KVX_SUCCESS;
   if (!layer_bases || !xfers || !xfer_count || !send_buf) return KVX_ERR_INVALID_ARGUMENT;
@@ -152,7 +172,8 @@ kvx_status kvx_unpack(const void* const* send_bufs, int32_t num_src, void* const
                       hipStream_t stream) {
   if (num_src < 1 || num_src > KVX_MAX_SOURCES || num_layers < 0 || block_bytes <= 0 ||
       num_cache_blocks < 0 || total_blocks < 0 || total_blocks > kMaxBlocks ||
-      rows_per_block < 1)
+      rows_per_block < 1 ||
+      !copy_extents_ok(num_layers, total_blocks, num_cache_blocks, block_bytes))
     return KVX_ERR_INVALID_ARGUMENT;
   if (!mult16(block_bytes)) return KVX_ERR_MISALIGNED;
   if (num_src > 1 && block_bytes % ((int64_t)rows_per_block * num_src * 16) != 0)
@@ -179,7 +200,9 @@ kvx_status kvx_copy_direct(void* const* src_layer_bases, void* const* dst_layer_
                            const int64_t* xfer_count, int64_t total_blocks, int32_t* err_flag,
                            hipStream_t stream) {
   if (num_layers < 0 || block_bytes <= 0 || src_num_blocks < 0 || dst_num_blocks < 0 ||
-      total_blocks < 0 || total_blocks > kMaxBlocks)
+      total_blocks < 0 || total_blocks > kMaxBlocks ||
+      !copy_extents_ok(num_layers, total_blocks, src_num_blocks, block_bytes) ||
+      !extent_ok(dst_num_blocks, block_bytes))
     return KVX_ERR_INVALID_ARGUMENT;
   if (num_layers == 0 || total_blocks == 0) return KVX_SUCCESS;
   if (!src_layer_bases || !dst_layer_bases || !xfers || !xfer_count || src_num_blocks == 0)
@@ -196,7 +219,8 @@ kvx_status kvx_pack_split(void* const* layer_bases, int32_t num_layers, int64_t 
                           const int64_t* xfer_count, int64_t total_blocks, void* const* send_bufs,
                           int32_t num_dst, int32_t* err_flag, hipStream_t stream) {
   if (num_dst < 1 || num_dst > KVX_MAX_SOURCES || num_layers < 0 || block_bytes <= 0 ||
-      num_cache_blocks < 0 || total_blocks < 0 || total_blocks > kMaxBlocks || rows_per_block < 1)
+      num_cache_blocks < 0 || total_blocks < 0 || total_blocks > kMaxBlocks || rows_per_block < 1 ||
+      !copy_extents_ok(num_layers, total_blocks, num_cache_blocks, block_bytes))
     return KVX_ERR_INVALID_ARGUMENT;
   if (!mult16(block_bytes)) return KVX_ERR_MISALIGNED;
   if (block_bytes % ((int64_t)rows_per_block * num_dst * 16) != 0) return KVX_ERR_INVALID_ARGUMENT;
@@ -225,7 +249,8 @@ kvx_status kvx_pack_signal(void* const* layer_bases, int32_t num_layers, int64_t
   const kvx_status sc = signal_checks(counter, arrivals);
   if (sc != KVX_SUCCESS) return sc;
   if (num_layers < 0 || block_bytes <= 0 || num_cache_blocks < 0 || total_blocks < 0 ||
-      total_blocks > kMaxBlocks)
+      total_blocks > kMaxBlocks ||
+      !copy_extents_ok(num_layers, total_blocks, num_cache_blocks, block_bytes))
     return KVX_ERR_INVALID_ARGUMENT;
   if (num_layers == 0 || total_blocks == 0)  // nothing to copy: the signal still goes out
     return from_hip(kvx::launch_signal_add(counter, delta, stream));
@@ -246,7 +271,9 @@ kvx_status kvx_copy_direct_signal(void* const* src_layer_bases, void* const* dst
   const kvx_status sc = signal_checks(counter, arrivals);
   if (sc != KVX_SUCCESS) return sc;
   if (num_layers < 0 || block_bytes <= 0 || src_num_blocks < 0 || dst_num_blocks < 0 ||
-      total_blocks < 0 || total_blocks > kMaxBlocks)
+      total_blocks < 0 || total_blocks > kMaxBlocks ||
+      !copy_extents_ok(num_layers, total_blocks, src_num_blocks, block_bytes) ||
+      !extent_ok(dst_num_blocks, block_bytes))
     return KVX_ERR_INVALID_ARGUMENT;
   if (num_layers == 0 || total_blocks == 0)
     return from_hip(kvx::launch_signal_add(counter, delta, stream));
@@ -269,7 +296,8 @@ kvx_status kvx_pack_signal_noalloc(void* const* layer_bases, int32_t num_layers,
   if (!counter) return KVX_ERR_INVALID_ARGUMENT;
   if (((uintptr_t)counter & 7u) != 0) return KVX_ERR_MISALIGNED;
   if (num_layers < 0 || block_bytes <= 0 || num_cache_blocks < 0 || total_blocks < 0 ||
-      total_blocks > kMaxBlocks)
+      total_blocks > kMaxBlocks ||
+      !copy_extents_ok(num_layers, total_blocks, num_cache_blocks, block_bytes))
     return KVX_ERR_INVALID_ARGUMENT;
   if (num_layers == 0 || total_blocks == 0)
     return from_hip(kvx::launch_signal_add(counter, delta, stream));
@@ -291,7 +319,9 @@ static kvx_status kv_first_checks(void* const* layer_bases, int32_t num_layers,
                                   const int64_t* xfer_count, int64_t total_blocks,
                                   const void* buffer) {
   if (num_layers < 0 || segment_bytes <= 0 || plane_stride_bytes < 0 || num_cache_blocks < 0 ||
-      total_blocks < 0 || total_blocks > kMaxBlocks || num_reqs < 0)
+      total_blocks < 0 || total_blocks > kMaxBlocks || num_reqs < 0 ||
+      !extent_ok(2, plane_stride_bytes) || !extent_ok(2, segment_bytes) ||
+      !extent_ok((int64_t)num_layers * total_blocks, 2 * segment_bytes))
     return KVX_ERR_INVALID_ARGUMENT;
   if (segment_bytes % 1024 != 0 || !mult16(plane_stride_bytes)) return KVX_ERR_MISALIGNED;
   // the V plane starts after the K plane's blocks (planes never overlap)

@@ -37,6 +37,7 @@ MODE_PACK, MODE_UNPACK, MODE_DIRECT = 0, 1, 2
 MAX_SOURCES = 8
 ARRIVALS_BYTES = 4096  # workspace of one signalling copy (KVX_ARRIVALS_BYTES)
 NOALLOC_SLOTS = 16  # arrivals workspaces the library keeps per GPU for kvx_pack_signal_noalloc
+MAX_EXTENT_BYTES = 1 << 56  # largest byte extent one call may describe (KVX_MAX_EXTENT_BYTES)
 XFER_BYTES = 32  # sizeof(kvx_xfer)
 
 _P = ctypes.c_void_p

@@ -34,7 +34,10 @@
  *     reads it after synchronising.
  *   - Results are bit-exact: all data is moved as raw bytes (no floating-point ops).
  *   - Block ids are int32; positions, slots, offsets and counts are int64; byte offsets are
- *     computed in 64-bit.
+ *     computed in 64-bit. Sizes that describe a byte extent past KVX_MAX_EXTENT_BYTES (a
+ *     cache's blocks x block bytes, a buffer's layers x blocks x block bytes, a count times
+ *     its stride) cannot be a real allocation and return KVX_ERR_INVALID_ARGUMENT, so that no
+ *     offset a kernel forms can overflow.
  */
 #ifndef KVX_H
 #define KVX_H
@@ -54,6 +57,9 @@ typedef enum kvx_status {
                                    request goes past the library's fixed scratch          */
   KVX_ERR_HIP = 4               /* the HIP launch failed                                */
 } kvx_status;
+
+/* Largest byte extent one call may describe (2^56 bytes, 64 PiB). */
+#define KVX_MAX_EXTENT_BYTES (1LL << 56)
 
 /* Device error bits OR-ed into *err_flag. */
 #define KVX_DEVERR_BLOCK_RANGE 1 /* a cache block id outside [0, num_cache_blocks)        */

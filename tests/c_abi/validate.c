@@ -251,6 +251,51 @@ int main(void) {
     expect("noalloc buf +8", noalloc(0, cnt, 2, 8192, P, AT(8)), KVX_ERR_MISALIGNED);
   }
 
+  /* byte extents past KVX_MAX_EXTENT_BYTES, including products that overflow 64 bits; an extent
+   * exactly at the limit passes that check and meets the next one */
+  {
+    const int64_t M = KVX_MAX_EXTENT_BYTES, bb = (int64_t)1 << 17, lim = M / bb;
+    const void* two[2] = {P, P};
+    void* twob[2] = {P, P};
+    expect("pack cache extent past the limit", pack(P, 2, bb, lim + 1, P, P, 10, P), KVX_ERR_INVALID_ARGUMENT);
+    expect("pack cache extent overflowing", pack(P, 2, 1024, (int64_t)1 << 62, P, P, 10, P),
+           KVX_ERR_INVALID_ARGUMENT);
+    expect("pack buffer extent past the limit", pack(P, 2, (int64_t)1 << 26, 100, P, P, (int64_t)1 << 30, P),
+           KVX_ERR_INVALID_ARGUMENT);
+    expect("pack cache extent at the limit", pack(P, 2, bb, lim, P, P, 10, AT(8)), KVX_ERR_MISALIGNED);
+    expect("unpack buffer extent past the limit",
+           kvx_unpack(two, 2, (void* const*)P, 2, (int64_t)1 << 26, 100, 32, (const kvx_xfer*)P,
+                      (const int64_t*)P, (int64_t)1 << 30, NUL, NUL),
+           KVX_ERR_INVALID_ARGUMENT);
+    expect("direct destination extent past the limit", direct(P, P, 2, bb, 100, lim + 1, P, 10),
+           KVX_ERR_INVALID_ARGUMENT);
+    expect("direct_signal source extent past the limit",
+           direct_signal(AT(1024), AT(2048), 2, bb, lim + 1, P, P, 10), KVX_ERR_INVALID_ARGUMENT);
+    expect("split cache extent past the limit",
+           kvx_pack_split((void* const*)P, 2, bb, lim + 1, 32, (const kvx_xfer*)P, (const int64_t*)P, 10, twob, 2,
+                          NUL, NUL),
+           KVX_ERR_INVALID_ARGUMENT);
+    expect("pack_signal cache extent overflowing",
+           kvx_pack_signal((void* const*)P, 2, 1024, (int64_t)1 << 62, (const kvx_xfer*)P, (const int64_t*)P, 10, P,
+                           (uint64_t*)AT(1024), 1, (uint32_t*)AT(2048), NUL, NUL),
+           KVX_ERR_INVALID_ARGUMENT);
+    expect("noalloc cache extent overflowing",
+           kvx_pack_signal_noalloc((void* const*)P, 2, 1024, (int64_t)1 << 62, (const kvx_xfer*)P, (const int64_t*)P,
+                                   10, P, (uint64_t*)AT(1024), 1, 0, NUL, NUL),
+           KVX_ERR_INVALID_ARGUMENT);
+    expect("kv-first plane past the limit", kvf(1, 4096, M, P, 2, 10, P), KVX_ERR_INVALID_ARGUMENT);
+    expect("kv-first buffer extent past the limit",
+           kvf(0, (int64_t)1 << 25, ((int64_t)1 << 25) * 100, P, 2, (int64_t)1 << 30, P), KVX_ERR_INVALID_ARGUMENT);
+    expect("slot mapping table extent past the limit", slots(8, (int64_t)1 << 55, 10, 16, P),
+           KVX_ERR_INVALID_ARGUMENT);
+    expect("write cache extent overflowing",
+           kvx_reshape_and_cache(P, 4096, P, 4096, 10, 2048, (const int64_t*)P, P, (int64_t)1 << 60, 16,
+                                 (int64_t)1 << 20, 4096, 2048, NUL, NUL),
+           KVX_ERR_INVALID_ARGUMENT);
+    expect("write row extent overflowing", write_rows(P, (int64_t)1 << 50, 2048, P, 16, 2048),
+           KVX_ERR_INVALID_ARGUMENT);
+  }
+
   printf("validated %d calls, %d mismatches\n", calls, failures);
   return failures ? 1 : 0;
 }

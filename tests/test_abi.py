@@ -276,6 +276,66 @@ def test_allocation_free_pack_validation(kvx):
     assert "scratch" in kvx.kvx_status_string(kvx.KVX_ERR_CAPACITY)
 
 
+def test_byte_extents_past_the_limit(kvx):
+    """Sizes whose byte extent passes KVX_MAX_EXTENT_BYTES (2^56) describe no real allocation;
+    every entry point refuses them before anything else could form an overflowing offset,
+    including products that overflow 64 bits. An extent exactly at the limit passes that check
+    and meets the next one (here a misaligned buffer)."""
+    M = 1 << 56
+    bb = 1 << 17
+    big_nb = M // bb + 1           # one block more than a cache at the limit
+    assert kvx.MAX_EXTENT_BYTES == M
+
+    def pack(fn="kvx_pack", nb=100, L=2, n=10, b=bb, buf=P):
+        if fn == "kvx_pack":
+            return call(kvx, fn, P, L, b, nb, P, P, n, buf, None, None)
+        if fn == "kvx_pack_signal":
+            return call(kvx, fn, P, L, b, nb, P, P, n, buf, 0x1000, 1, 0x2000, None, None)
+        return call(kvx, fn, P, L, b, nb, P, P, n, buf, 0x1000, 1, 0, None, None)
+    for fn in ("kvx_pack", "kvx_pack_signal", "kvx_pack_signal_noalloc"):
+        assert pack(fn, nb=big_nb) == kvx.KVX_ERR_INVALID_ARGUMENT, fn
+        assert pack(fn, nb=1 << 62, b=1 << 10) == kvx.KVX_ERR_INVALID_ARGUMENT, fn  # overflows int64
+        assert pack(fn, L=2, n=1 << 30, b=1 << 26) == kvx.KVX_ERR_INVALID_ARGUMENT, fn  # buffer: 2^57
+        assert pack(fn, nb=M // bb, buf=P + 8) == kvx.KVX_ERR_MISALIGNED, fn  # exactly at the limit
+
+    def unpack(nb=100, n=10, b=bb, S=1):
+        arr = (ctypes.c_void_p * S)(*([P] * S))
+        return call(kvx, "kvx_unpack", arr, S, P, 2, b, nb, 32, P, P, n, None, None)
+    assert unpack(nb=big_nb) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert unpack(nb=big_nb, S=2) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert unpack(n=1 << 30, b=1 << 26) == kvx.KVX_ERR_INVALID_ARGUMENT
+
+    def direct(fn, nbs=100, nbd=100):
+        if fn == "kvx_copy_direct":
+            return call(kvx, fn, P, P, 2, bb, nbs, nbd, P, P, 10, None, None)
+        return call(kvx, fn, P, P, 2, bb, nbs, nbd, P, P, 10, 0x1000, 1, 0x2000, None, None)
+    for fn in ("kvx_copy_direct", "kvx_copy_direct_signal"):
+        assert direct(fn, nbs=big_nb) == kvx.KVX_ERR_INVALID_ARGUMENT, fn
+        assert direct(fn, nbd=big_nb) == kvx.KVX_ERR_INVALID_ARGUMENT, fn
+
+    arr = (ctypes.c_void_p * 2)(P, P)
+    assert call(kvx, "kvx_pack_split", P, 2, bb, big_nb, 32, P, P, 10, arr, 2, None, None) == \
+        kvx.KVX_ERR_INVALID_ARGUMENT
+
+    for fn in ("kvx_pack_kv_first", "kvx_unpack_kv_first"):
+        def kvf(seg=4096, plane=4096 * 100, n=10):
+            if fn == "kvx_pack_kv_first":
+                return call(kvx, fn, P, 2, seg, plane, 100, P, 2, P, P, n, P, None, None)
+            return call(kvx, fn, P, P, 2, seg, plane, 100, P, 2, P, P, n, None, None)
+        assert kvf(plane=M) == kvx.KVX_ERR_INVALID_ARGUMENT, fn      # the V plane ends past 2^56
+        assert kvf(n=1 << 30, seg=1 << 25, plane=(1 << 25) * 100) == kvx.KVX_ERR_INVALID_ARGUMENT, fn
+
+    assert call(kvx, "kvx_slot_mapping", P, 4, 8, 1 << 55, P, P, 10, 16, P, None, None) == \
+        kvx.KVX_ERR_INVALID_ARGUMENT
+
+    def rc(T=10, nb=64, bst=65536, ks=4096):
+        return call(kvx, "kvx_reshape_and_cache", P, ks, P, 4096, T, 2048, P, P, nb, 16, bst, 4096, 2048,
+                    None, None)
+    assert rc(nb=1 << 41) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert rc(nb=1 << 60, bst=1 << 20) == kvx.KVX_ERR_INVALID_ARGUMENT
+    assert rc(T=1 << 50, ks=1 << 10) == kvx.KVX_ERR_INVALID_ARGUMENT
+
+
 def _run_python(code, env_extra=None):
     import subprocess
     import sys

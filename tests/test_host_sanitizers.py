@@ -1,5 +1,6 @@
 """The library's host-side argument checks under AddressSanitizer and UndefinedBehaviorSanitizer.
-tests/c_abi/validate.c calls every entry point with invalid and empty arguments (119 calls)
+tests/c_abi/validate.c calls every entry point with invalid and empty arguments, and with byte
+extents past the library's limit (134 calls),
 against a build whose host code is instrumented: every status must match what the header
 documents, and neither sanitizer may report. Host code only; no GPU is needed."""
 import importlib.util
@@ -24,5 +25,5 @@ def test_argument_validation_under_sanitizers():
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120, env=env)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert "validated 119 calls, 0 mismatches" in r.stdout, r.stdout
+    assert "validated 134 calls, 0 mismatches" in r.stdout, r.stdout
     assert "runtime error" not in r.stderr and "Sanitizer" not in r.stderr, r.stderr
