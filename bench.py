@@ -30,7 +30,7 @@ a graph is fixed to one transfer size).
 
     python bench.py [--steps K] [--warmup W] [--workload contiguous|fragmented]
                     [--no-cpu-baseline] [--no-ops] [--no-pipeline] [--no-graph] [--copy-calib]
-                    [--alloc-spread ROUNDS]
+                    [--alloc-spread ROUNDS] [--tiny]
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
@@ -79,6 +79,8 @@ def parse():
                     help="skip timing the step replayed from a captured HIP graph (graph_ms_per_step)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--tiny", action="store_true",
+                    help="only time the smallest transfer (ops.tiny_transfer), e.g. under a kernel trace")
     ap.add_argument("--alloc-spread", type=int, default=0, metavar="ROUNDS",
                     help="only measure how rates move with where the destination caches sit in memory: "
                          "ROUNDS placements of the 48-layer receive caches and the asymmetric-TP destination "
@@ -211,6 +213,9 @@ def main():
         return
     if args.alloc_spread:
         alloc_spread(torch, np, W, K, dev, args.alloc_spread)
+        return
+    if args.tiny:
+        print(json.dumps({"tiny_transfer": tiny_transfer(torch, np, W, K, dev)}), flush=True)
         return
 
     case = W.pages_contiguous() if args.workload == "contiguous" else W.pages_fragmented()
