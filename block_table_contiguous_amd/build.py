@@ -64,7 +64,10 @@ def build(asm_dir: str | None = None, verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
+    # --asm [DIR]: also write each source's gfx950 assembly (default: _build/asm beside this file)
     asm = None
     if "--asm" in sys.argv:
-        asm = os.path.join(ROOT, "_work", "asm")
+        i = sys.argv.index("--asm")
+        given = sys.argv[i + 1] if i + 1 < len(sys.argv) and not sys.argv[i + 1].startswith("-") else None
+        asm = given or os.path.join(os.path.dirname(os.path.abspath(__file__)), "_build", "asm")
     print(build(asm_dir=asm, verbose=True))
